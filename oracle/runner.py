@@ -1,0 +1,69 @@
+"""Run one synthetic decode step entirely on the oracle side.
+
+Drives the oracle block manager through the workload's ops, writes every prior
+token and the new tokens with ``scatter_ref``, applies the copy-on-write pairs
+with ``copy_ref`` and evaluates ``paged_decode_ref``.  Test infrastructure only.
+"""
+
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .attention import paged_decode_ref
+from .block_manager import BlockManager
+from .cache_ops import copy_ref, new_cache, scatter_ref
+
+BLOCK_SIZE = 16
+
+
+@dataclass
+class OracleStep:
+    block_manager: BlockManager
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    k_cache_before_step: Optional[np.ndarray]
+    v_cache_before_step: Optional[np.ndarray]
+    slot_mapping: np.ndarray
+    block_pairs: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    out: Optional[np.ndarray]  # float64 [S, Hq, D]
+
+
+def run_decode_step(wl, *, max_blocks: Optional[int] = None, compute_out: bool = True,
+                    keep_before: bool = False, seqs: Optional[Sequence[int]] = None) -> OracleStep:
+    hkv = wl.num_kv_heads
+    npdt = {"fp16": np.float16, "bf16": np.uint16}[wl.dtype]
+    bm = BlockManager(wl.pool_blocks, BLOCK_SIZE, wl.free_order)
+    kc, vc = new_cache(wl.pool_blocks, BLOCK_SIZE, hkv, 128, npdt)
+    slot_mapping = pairs = None
+    kb = vb = None
+    for op in wl.ops:
+        if op[0] == "add":
+            _, s, n = op
+            slots = bm.add(s, n)
+            if n:
+                k, v = wl.prior_kv_for_add(s)
+                scatter_ref(kc, vc, k, v, slots)
+        elif op[0] == "fork":
+            bm.fork(op[1], op[2])
+        elif op[0] == "step":
+            if keep_before:
+                kb, vb = kc.copy(), vc.copy()
+            slot_mapping, pairs = bm.step(op[1])
+            copy_ref(kc, vc, pairs)
+            k_new, v_new = wl.new_token_kv()
+            scatter_ref(kc, vc, k_new, v_new, slot_mapping)
+        else:
+            raise ValueError(op)
+    S = wl.num_seqs
+    ctx = bm.context_lens(range(S))
+    assert np.array_equal(ctx, wl.context_lens)
+    if max_blocks is None:
+        max_blocks = max(len(bm.blocks[s]) for s in range(S))
+    tables = bm.block_table(range(S), max_blocks)
+    out = None
+    if compute_out:
+        out = paged_decode_ref(wl.q, kc, vc, tables, ctx, wl.scale, hkv, wl.dtype, seqs=seqs)
+    return OracleStep(bm, kc, vc, kb, vb, slot_mapping, pairs, tables, ctx, out)

@@ -1,0 +1,360 @@
+"""Seeded synthetic workloads for paged decode attention.
+
+This module only draws random numbers and describes workloads. It holds none of
+the method's arithmetic: no attention, no paging, no slot or block-table math.
+Both the oracle side (``oracle/``) and the HIP side (the package binding) take
+their inputs from here, and nothing else is shared between them.
+
+Workload shapes follow the five decode batches the paged-attention pages are
+measured on (LLaMA-7B/13B-shaped serving batches, a GQA batch, a long-context
+split batch, and a tiny case).  The pages' own workload draws prompt and output
+lengths from ShareGPT, which is not available; the lognormal and uniform length
+recipes below stand in for it.
+
+Recipe (all streams are ``numpy.random.default_rng``):
+
+* main stream ``default_rng(seed)``: context lengths first, then a permutation
+  of the block pool (the free-list order), then per-KV-head key scales (GQA
+  batch only), then the query ``[S, Hq, D]``;
+* per-sequence stream ``default_rng([seed, 1, s])``: K then V rows of the tokens
+  that belong to sequence ``s`` alone (all its tokens for a singleton, only the
+  new token for a member of a sampling group);
+* per-group stream ``default_rng([seed, 2, g])``: K then V rows of the shared
+  prompt of sampling group ``g``.
+
+Values are drawn N(0, 1) in float32 and rounded once, round-to-nearest-even, to
+the storage dtype; both sides receive the rounded values.  bfloat16 values are
+kept as their uint16 bit patterns because numpy has no bfloat16 type.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+HEAD_SIZE = 128
+BLOCK_SIZE = 16
+
+__all__ = [
+    "HEAD_SIZE",
+    "BLOCK_SIZE",
+    "ConfigSpec",
+    "CONFIGS",
+    "Workload",
+    "make_workload",
+    "make_random_workload",
+    "round_fp16",
+    "round_bf16_bits",
+    "storage_dtype",
+    "thread_map",
+]
+
+
+def thread_map(fn, items, max_workers: Optional[int] = None):
+    """map() over a thread pool; numpy's generators release the GIL while
+    filling large arrays, so per-sequence draws run in parallel."""
+    items = list(items)
+    if max_workers is None:
+        max_workers = min(16, len(os.sched_getaffinity(0)))
+    if max_workers <= 1 or len(items) <= 1:
+        return [fn(i) for i in items]
+    with ThreadPoolExecutor(max_workers) as ex:
+        return list(ex.map(fn, items))
+
+
+# --------------------------------------------------------------------------
+# rounding of float32 draws to the storage dtype (input encoding only)
+# --------------------------------------------------------------------------
+
+def round_fp16(x: np.ndarray) -> np.ndarray:
+    """float32 -> float16, round to nearest even (numpy's cast)."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16)
+
+
+def round_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    Inputs are finite by construction, so no NaN special case is needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # finite inputs: u + 0x8000 cannot wrap past 0xFFFFFFFF
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def storage_dtype(dtype: str):
+    if dtype == "fp16":
+        return np.float16
+    if dtype == "bf16":
+        return np.uint16
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    return round_fp16(x) if dtype == "fp16" else round_bf16_bits(x)
+
+
+# --------------------------------------------------------------------------
+# configurations
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class ConfigSpec:
+    name: str
+    seed: int
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    dtype: str
+    lengths: Tuple  # ("fixed", [...]) | ("lognormal", median, sigma, cap) | ("uniform", lo, hi)
+    pool_blocks: int  # physical pool size (1.1x the blocks the batch needs; C1: 64)
+    group_fraction: float = 0.0  # fraction of sequences in sampling groups of 3
+    key_scale: Optional[Tuple[float, float]] = None  # per-KV-head U[lo, hi] key scale
+    partition_tokens: int = 0  # 0: library default
+    description: str = ""
+
+    @property
+    def group_size(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(HEAD_SIZE)
+
+
+CONFIGS: Dict[str, ConfigSpec] = {
+    "tiny": ConfigSpec(
+        name="tiny", seed=1, num_seqs=4, num_heads=8, num_kv_heads=8, dtype="fp16",
+        lengths=("fixed", (17, 33, 100, 250)), pool_blocks=64,
+        description="4 sequences, contexts {17,33,100,250}, 8/8 heads, fp16, 64-block pool"),
+    "llama7b": ConfigSpec(
+        name="llama7b", seed=2, num_seqs=64, num_heads=32, num_kv_heads=32, dtype="fp16",
+        lengths=("lognormal", 400.0, 1.0, 2048), pool_blocks=2731,
+        description="LLaMA-7B-shaped decode batch: 64 seqs, 32 MHA heads, fp16, "
+                    "lognormal contexts (median 400, cap 2048), pool 1.1x"),
+    "llama13b": ConfigSpec(
+        name="llama13b", seed=3, num_seqs=128, num_heads=40, num_kv_heads=40, dtype="fp16",
+        lengths=("lognormal", 600.0, 1.0, 2048), pool_blocks=5548, group_fraction=0.3,
+        description="LLaMA-13B-shaped decode batch: 128 seqs, 40 MHA heads, fp16, "
+                    "lognormal contexts (median 600, cap 2048), 13 groups of 3 "
+                    "parallel samples sharing prompt blocks, copy-on-write"),
+    "gqa": ConfigSpec(
+        name="gqa", seed=4, num_seqs=256, num_heads=64, num_kv_heads=8, dtype="bf16",
+        lengths=("uniform", 1024, 8192), pool_blocks=83223, key_scale=(0.5, 2.0),
+        description="GQA decode batch: 256 seqs, 64 query / 8 KV heads, bf16, "
+                    "contexts U[1024,8192], per-KV-head key scale U[0.5,2]"),
+    "long": ConfigSpec(
+        name="long", seed=5, num_seqs=8, num_heads=32, num_kv_heads=8, dtype="bf16",
+        lengths=("uniform", 32768, 131072), pool_blocks=46457, partition_tokens=512,
+        description="long-context split decode: 8 seqs, 32 query / 8 KV heads, bf16, "
+                    "contexts U[32768,131072], 512-token partitions"),
+}
+
+
+# --------------------------------------------------------------------------
+# workload
+# --------------------------------------------------------------------------
+
+@dataclass
+class Workload:
+    """A decode step: each sequence has ``context_lens[s] - 1`` tokens already in
+    the cache and appends one new token, whose K/V is written through the slot
+    mapping before attention reads all ``context_lens[s]`` tokens.
+
+    ``ops`` describes the block-manager calls that build this state, in order:
+      ("add", seq, n_tokens)   a new sequence with n_tokens prior tokens
+      ("fork", parent, child)  child shares all of parent's blocks
+      ("step", [seq, ...])     append one token to each listed sequence
+    """
+
+    spec: ConfigSpec
+    context_lens: np.ndarray  # int64 [S]
+    free_order: np.ndarray  # int32 [pool]
+    q: np.ndarray  # storage dtype [S, Hq, D]
+    key_scales: Optional[np.ndarray]  # float32 [Hkv] or None
+    groups: List[Tuple[int, int, int]]  # (first_seq, n_samples, prompt_len)
+    ops: List[tuple] = field(default_factory=list)
+
+    # ---- shape helpers -------------------------------------------------
+    @property
+    def num_seqs(self) -> int:
+        return self.spec.num_seqs
+
+    @property
+    def num_heads(self) -> int:
+        return self.spec.num_heads
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.spec.num_kv_heads
+
+    @property
+    def dtype(self) -> str:
+        return self.spec.dtype
+
+    @property
+    def pool_blocks(self) -> int:
+        return int(self.free_order.shape[0])
+
+    @property
+    def scale(self) -> float:
+        return self.spec.scale
+
+    def group_of(self, s: int) -> Optional[int]:
+        for g, (first, n, _p) in enumerate(self.groups):
+            if first <= s < first + n:
+                return g
+        return None
+
+    # ---- value streams ---------------------------------------------------
+    def _draw_kv(self, rng: np.random.Generator, n: int):
+        hkv = self.num_kv_heads
+        k = rng.standard_normal((n, hkv, HEAD_SIZE), dtype=np.float32)
+        if self.key_scales is not None:
+            k *= self.key_scales[None, :, None]
+        v = rng.standard_normal((n, hkv, HEAD_SIZE), dtype=np.float32)
+        return _to_storage(k, self.dtype), _to_storage(v, self.dtype)
+
+    def group_prompt_kv(self, g: int):
+        _first, _n, plen = self.groups[g]
+        rng = np.random.default_rng([self.spec.seed, 2, g])
+        return self._draw_kv(rng, plen)
+
+    def own_kv(self, s: int):
+        """K/V rows that belong to sequence s alone (all of them for a
+        singleton, only the newly decoded token for a group member)."""
+        g = self.group_of(s)
+        n = 1 if g is not None else int(self.context_lens[s])
+        rng = np.random.default_rng([self.spec.seed, 1, s])
+        return self._draw_kv(rng, n)
+
+    def seq_kv(self, s: int):
+        """Contiguous K/V of all context_lens[s] tokens of sequence s, in
+        logical order: [L_s, Hkv, D] each (storage dtype)."""
+        g = self.group_of(s)
+        k_own, v_own = self.own_kv(s)
+        if g is None:
+            return k_own, v_own
+        k_p, v_p = self.group_prompt_kv(g)
+        return np.concatenate([k_p, k_own]), np.concatenate([v_p, v_own])
+
+    def new_token_kv(self):
+        """K/V of the token each sequence appends in the step: [S, Hkv, D]."""
+        ks, vs = [], []
+        for s in range(self.num_seqs):
+            k, v = self.own_kv(s)
+            ks.append(k[-1])
+            vs.append(v[-1])
+        return np.stack(ks), np.stack(vs)
+
+    def prior_kv_for_add(self, seq: int):
+        """K/V of the prior tokens created by the ("add", seq, n) op."""
+        g = self.group_of(seq)
+        if g is not None:
+            return self.group_prompt_kv(g)
+        k, v = self.own_kv(seq)
+        n = int(self.context_lens[seq]) - 1
+        return k[:n], v[:n]
+
+    @property
+    def total_context(self) -> int:
+        return int(self.context_lens.sum())
+
+
+def _draw_lengths(spec: ConfigSpec, rng: np.random.Generator):
+    kind = spec.lengths[0]
+    S = spec.num_seqs
+    groups: List[Tuple[int, int, int]] = []
+    if kind == "fixed":
+        lens = np.asarray(spec.lengths[1], dtype=np.int64)
+        assert lens.shape[0] == S
+        return lens, groups
+    if kind == "lognormal":
+        _, median, sigma, cap = spec.lengths
+        n_groups = int(round(spec.group_fraction * S / 3))
+        if n_groups:
+            plen = rng.lognormal(math.log(median), sigma, n_groups)
+            plen = np.clip(np.rint(plen), 1, cap - 1).astype(np.int64)
+        n_single = S - 3 * n_groups
+        x = rng.lognormal(math.log(median), sigma, n_single)
+        single = np.clip(np.rint(x), 1, cap).astype(np.int64)
+        lens = []
+        for g in range(n_groups):
+            groups.append((3 * g, 3, int(plen[g])))
+            lens += [int(plen[g]) + 1] * 3
+        lens += [int(v) for v in single]
+        return np.asarray(lens, dtype=np.int64), groups
+    if kind == "uniform":
+        _, lo, hi = spec.lengths
+        return rng.integers(lo, hi, S, endpoint=True).astype(np.int64), groups
+    raise ValueError(kind)
+
+
+def _ops_for(lens: np.ndarray, groups: Sequence[Tuple[int, int, int]]) -> List[tuple]:
+    ops: List[tuple] = []
+    S = int(lens.shape[0])
+    member = {}
+    for first, n, plen in groups:
+        for i in range(n):
+            member[first + i] = (first, plen)
+    for s in range(S):
+        if s in member:
+            first, plen = member[s]
+            if s == first:
+                ops.append(("add", s, plen))
+            else:
+                ops.append(("fork", first, s))
+        else:
+            ops.append(("add", s, int(lens[s]) - 1))
+    ops.append(("step", list(range(S))))
+    return ops
+
+
+def make_workload(name_or_spec, *, with_q: bool = True) -> Workload:
+    spec = CONFIGS[name_or_spec] if isinstance(name_or_spec, str) else name_or_spec
+    rng = np.random.default_rng(spec.seed)
+    lens, groups = _draw_lengths(spec, rng)
+    free_order = rng.permutation(spec.pool_blocks).astype(np.int32)
+    key_scales = None
+    if spec.key_scale is not None:
+        lo, hi = spec.key_scale
+        key_scales = rng.uniform(lo, hi, spec.num_kv_heads).astype(np.float32)
+    q = None
+    if with_q:
+        q = _to_storage(
+            rng.standard_normal((spec.num_seqs, spec.num_heads, HEAD_SIZE), dtype=np.float32),
+            spec.dtype)
+    return Workload(spec=spec, context_lens=lens, free_order=free_order, q=q,
+                    key_scales=key_scales, groups=groups, ops=_ops_for(lens, groups))
+
+
+def make_random_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_heads: int,
+                         dtype: str, max_len: int, pool_slack: int = 4,
+                         min_len: int = 1, groups: int = 0, key_scale=None) -> Workload:
+    """Small random workload for property tests: lengths U[min_len, max_len],
+    optionally the first 3*groups sequences in sampling groups of 3."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(min_len, max_len, num_seqs, endpoint=True).astype(np.int64)
+    grp = []
+    for g in range(groups):
+        plen = int(max(1, min(lens[3 * g], max_len) - 1))
+        grp.append((3 * g, 3, plen))
+        lens[3 * g:3 * g + 3] = plen + 1
+    # generous pool: every token its own block would still fit
+    pool = int(sum(-(-int(v) // BLOCK_SIZE) + 1 for v in lens)) + 3 * groups + pool_slack
+    spec = ConfigSpec(name=f"random{seed}", seed=seed, num_seqs=num_seqs, num_heads=num_heads,
+                      num_kv_heads=num_kv_heads, dtype=dtype,
+                      lengths=("fixed", tuple(int(v) for v in lens)), pool_blocks=pool,
+                      key_scale=key_scale)
+    free_order = rng.permutation(pool).astype(np.int32)
+    key_scales = None
+    if key_scale is not None:
+        key_scales = rng.uniform(key_scale[0], key_scale[1], num_kv_heads).astype(np.float32)
+    q = _to_storage(rng.standard_normal((num_seqs, num_heads, HEAD_SIZE), dtype=np.float32), dtype)
+    return Workload(spec=spec, context_lens=lens, free_order=free_order, q=q,
+                    key_scales=key_scales, groups=grp, ops=_ops_for(lens, grp))
