@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV cache hot path on one MI355X.
+
+One step = the three GPU calls of a decode step over one synthetic batch with
+every input already resident in HBM: copy_blocks (copy-on-write pairs),
+reshape_and_cache (the new tokens) and paged_attn_decode (split into
+partitions and merged by the log-sum-exp reduce when a row spans several).
+Default workload: the LLaMA-13B-shaped batch (128 sequences, 40 MHA heads,
+head 128, block 16, fp16, lognormal contexts with median 600 capped at 2048,
+13 groups of 3 parallel samples sharing prompt blocks).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--cpu-seconds S]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes(wl, step):
+    """Algorithmic bytes of one step (see the design doc for the accounting)."""
+    import numpy as np
+
+    eb = 2
+    hkv, hq, D = wl.num_kv_heads, wl.num_heads, 128
+    S = wl.num_seqs
+    lens = wl.context_lens.astype(np.int64)
+    per_token = 2 * hkv * D * eb  # K and V rows of one token, all KV heads
+    tables = step.block_tables_host
+    live = set()
+    for s in range(S):
+        L = int(lens[s])
+        for j in range(-(-L // 16)):
+            b = int(tables[s, j])
+            for t in range(min(16, L - 16 * j)):
+                live.add(b * 16 + t)
+    kv_seq = int(lens.sum()) * per_token
+    kv_unique = len(live) * per_token
+    nblk = int(sum(-(-int(L) // 16) for L in lens))
+    qo = 2 * S * hq * D * eb
+    meta = nblk * 4 + S * 4
+    decode = kv_unique + qo + meta
+    n_pairs = int(step.block_pairs_host.shape[0])
+    copy = n_pairs * 2 * hkv * 2048 * eb * 2  # K and V pages of every head, read + write
+    T = int(step.slot_mapping_host.shape[0])
+    write = T * hkv * D * eb * 2 * 2 + T * 4  # K and V rows read + written, slots read
+    return dict(kv_per_sequence=kv_seq, kv_unique=kv_unique, decode=decode, copy=copy, write=write,
+                step=decode + copy + write, q_out=qo, meta=meta)
+
+
+def cpu_baseline(wl, seconds: float):
+    """The fp64 oracle's paged decode on the host cores, timed on a bounded
+    prefix of the batch's sequences (setup and data generation untimed)."""
+    import numpy as np
+
+    import oracle
+
+    log("cpu baseline: building the oracle's cache (untimed)")
+    ref = oracle.run_decode_step(wl, compute_out=False)
+    per_token = 2 * wl.num_kv_heads * 128 * 2
+    done, nbytes, wall, cpu = [], 0, 0.0, 0.0
+    for s in range(wl.num_seqs):
+        t0, c0 = time.perf_counter(), time.process_time()
+        oracle.paged_decode_ref(wl.q, ref.k_cache, ref.v_cache, ref.block_tables, ref.context_lens, wl.scale,
+                                wl.num_kv_heads, wl.dtype, seqs=[s])
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        done.append(s)
+        nbytes += int(wl.context_lens[s]) * per_token
+        if wall >= seconds:
+            break
+    return {
+        "value": round(nbytes / wall / 1e9, 4),
+        "unit": "GB/s",
+        "cores": max(1, int(round(cpu / wall))),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy paged decode of sequences 0..{done[-1]} ({len(done)} of {wl.num_seqs}, "
+                   f"{int(np.asarray(wl.context_lens)[done].sum())} context tokens, all {wl.num_heads} heads) "
+                   f"in {wall:.1f} s; per-sequence KV bytes / wall time"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "host_cpu_model": platform.processor() or platform.machine(),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama13b")
+    ap.add_argument("--partition-tokens", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("this build runs on one GPU only: the decode hot path is measured on a single MI355X "
+               "(no multi-GPU sharding is implemented); run with --gpus 1")
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(msg, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import harness
+    import paged_kv_cache_345_amd as pkv
+    import synth
+
+    if not os.path.exists(pkv.LIB_PATH):
+        from paged_kv_cache_345_amd.build import build
+        build()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+
+    wl = synth.make_workload(args.workload)
+    log(f"workload {wl.spec.name}: {wl.spec.description}")
+    t0 = time.perf_counter()
+    step = harness.build_step(wl, partition_tokens=args.partition_tokens)
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t0:.1f} s (partition {pkv.partition_tokens_for(wl.num_seqs, wl.num_heads, step.max_blocks, step.desc, step.partition_tokens)} tokens)")
+    nb = step_bytes(wl, step)
+
+    for _ in range(args.warmup):
+        step.run_step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    dec_start = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    dec_end = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    all_start = torch.cuda.Event(enable_timing=True)
+    all_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    all_start.record()
+    for i in range(K):
+        step.copy()
+        step.write()
+        dec_start[i].record()
+        step.decode()
+        dec_end[i].record()
+    all_end.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - w0
+    ms_per_step = all_start.elapsed_time(all_end) / K
+    dec_ms = [a.elapsed_time(b) for a, b in zip(dec_start, dec_end)]
+    dec_avg = float(np.mean(dec_ms))
+    log(f"step {ms_per_step * 1e3:.1f} us (wall {wall_s / K * 1e6:.1f} us); decode avg {dec_avg * 1e3:.1f} us, "
+        f"min {min(dec_ms) * 1e3:.1f} us")
+
+    step_gbs = nb["step"] / (ms_per_step * 1e-3) / 1e9
+    dec_gbs = nb["decode"] / (dec_avg * 1e-3) / 1e9
+    S = wl.num_seqs
+    result = {
+        "metric": "paged decode-attention KV GB/s (% of MI355X HBM peak) and tokens/s at 1 GPU",
+        "value": round(step_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.spec.description,
+            "name": wl.spec.name,
+            "num_seqs": S,
+            "num_heads": wl.num_heads,
+            "num_kv_heads": wl.num_kv_heads,
+            "head_size": 128,
+            "block_size": 16,
+            "context_tokens": wl.total_context,
+            "partition_tokens": pkv.partition_tokens_for(S, wl.num_heads, step.max_blocks, step.desc,
+                                                         step.partition_tokens),
+            "copy_pairs": int(step.block_pairs_host.shape[0]),
+            "step": "copy_blocks + reshape_and_cache + paged_attn_decode",
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "context_tokens_per_s": round(wl.total_context / (ms_per_step * 1e-3), 1),
+        "bytes": nb,
+        "decode_call_us": round(dec_avg * 1e3, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attn_decode (decode kernel + log-sum-exp reduce)",
+            "achieved": round(dec_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,229 @@
+/*
+ * pagedkv.h — C ABI of libpagedkv.so: paged decode attention for gfx950 (MI355X).
+ *
+ * The operations follow the PagedAttention mechanism described on these pages:
+ *   [blog]  "vLLM 部署与 PagedAttention 原理 · 检索整理（CSDN 频道批次）", item 2
+ *           (the 2023 vLLM blog): the KV cache is cut into fixed-size token
+ *           blocks reached through a per-sequence block table; blocks are taken
+ *           on demand, so only the last block of a sequence wastes space;
+ *           reference counts and copy-on-write let parallel samples share
+ *           prompt blocks.
+ *   [repo]  "vLLM 深度解析：以 PagedAttention 与内核生态构建高吞吐 LLM 推理引擎",
+ *           §2.1 PagedAttention: a block holds BLOCK_SIZE tokens of one head
+ *           (16 x 128 = 2048 elements); the kernel computes QK dot products, a
+ *           softmax normalisation and the weighted accumulation of V.
+ *   [stack] "vLLM：从 PagedAttention 长出来的开源服务栈，200+ 模型架构与五维并行",
+ *           section "把显存当虚拟内存管": logical-to-physical block mapping,
+ *           non-contiguous physical blocks, waste confined to the last block.
+ *
+ * Conventions for every function below:
+ *   - Data pointers are DEVICE pointers unless marked "host".  Bases must be
+ *     16-byte aligned (256-byte alignment recommended).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     device work is enqueued asynchronously on it; the library never
+ *     synchronises, never allocates device memory and keeps no state between
+ *     calls (the block manager object is the one host-side exception).
+ *   - Argument errors a host can see are reported by the return value BEFORE
+ *     anything is launched.  The library never aborts or throws across the ABI.
+ *   - Contents of device arrays (block ids, slots, context lengths) are the
+ *     caller's contract and are not checked on the fast path.  Values outside
+ *     the pool never cause an out-of-bounds access: a block id outside
+ *     [0, num_blocks) is treated as an all-masked block and an out-of-range
+ *     slot or block pair is skipped.
+ *
+ * KV page layout (element offsets; one element = 2 bytes).  k_cache and v_cache
+ * are separate buffers of pkv_cache_bytes() each.  Page (b, h) — block b, KV
+ * head h — starts at element (b * num_kv_heads + h) * 2048.  Inside a page,
+ * token t in [0,16) and dimension d in [0,128):
+ *   K: (d / 8) * 128 + t * 8 + (d % 8)
+ *   V: ((d / 16) / 2) * 512 + (16 * (t / 4) + d % 16) * 8 + ((d / 16) % 2) * 4 + t % 4
+ * (integer division).  With these, each 64-lane wave reads a page as four fully
+ * contiguous 1 KiB loads of 16 bytes per lane, and the bytes a lane receives
+ * are the operand fragments of the 16x16x32 (K) and 16x16x16 (V) matrix-core
+ * instructions; see pkv_k_index / pkv_v_index.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = 1,       /* bad argument: null pointer, bad count, small workspace, ... */
+  PKV_ERR_UNSUPPORTED = 2,   /* block_size != 16, head_size != 128, unknown dtype */
+  PKV_ERR_DEVICE = 3,        /* a HIP launch or runtime call failed */
+  PKV_ERR_OUT_OF_BLOCKS = 4  /* block manager: the free list cannot cover the request */
+} pkv_status;
+
+typedef enum { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Shape of one layer's paged KV cache. */
+typedef struct {
+  int32_t num_blocks;   /* physical pool size */
+  int32_t block_size;   /* tokens per block; must be 16 */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_size;    /* must be 128 */
+  int32_t dtype;        /* pkv_dtype of the cache, of q/out and of new k/v */
+} pkv_cache_desc;
+
+/* Bytes of ONE of k_cache / v_cache: num_blocks * num_kv_heads * 2048 * 2.
+ * Returns 0 for an invalid or unsupported descriptor. */
+size_t pkv_cache_bytes(const pkv_cache_desc* cache);
+
+/* Element offset of (block, head, token, dim) inside k_cache / v_cache, from the
+ * layout formulas above.  -1 on out-of-range arguments.  Host-only helpers. */
+int64_t pkv_k_index(const pkv_cache_desc* cache, int32_t block, int32_t head, int32_t token, int32_t dim);
+int64_t pkv_v_index(const pkv_cache_desc* cache, int32_t block, int32_t head, int32_t token, int32_t dim);
+
+/* ---------------------------------------------------------------------------
+ * paged_attn_decode — one query token per sequence attends to all
+ * context_lens[s] tokens of its sequence ([repo] §2.1: QK dot products,
+ * softmax normalisation, weighted sum of V), reading K/V pages through the
+ * block table ([blog] item 2, [stack]).
+ *
+ *   out[s, h, :] = sum_t softmax_t(scale * q[s,h,:] . K[s,t,kvh,:]) * V[s,t,kvh,:]
+ *   with kvh = h / (num_heads / num_kv_heads) and t < context_lens[s].
+ *
+ *   out           [num_seqs, num_heads, 128]   cache dtype, written (round to nearest even)
+ *   q             [num_seqs, num_heads, 128]   cache dtype
+ *   k_cache/v_cache                            pages as documented above
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq], row-major; entry j of
+ *                 row s is the physical block of tokens 16j..16j+15.  Entries
+ *                 at j >= ceil(context_lens[s] / 16) are never read.
+ *   context_lens  int32 [num_seqs]; 1 <= context_lens[s] <= 16*max_blocks_per_seq
+ *                 (a length of 0 yields a zero output row; longer lengths are
+ *                 clamped to the table).
+ *   scale         multiplies the logits before the softmax.
+ *   num_kv_heads  must equal cache->num_kv_heads and divide num_heads.
+ *   partition_tokens  0 = automatic; otherwise a multiple of 16 in [16, 1024]:
+ *                 each sequence's context is split into partitions of this many
+ *                 tokens whose softmax statistics are merged by a log-sum-exp
+ *                 reduce kernel.
+ *   workspace     device scratch of at least paged_attn_decode_workspace_size()
+ *                 bytes (may be NULL when that size is 0).  Owned by the caller;
+ *                 contents on entry are irrelevant.
+ * Calls on one stream are ordered; two calls sharing a workspace on different
+ * streams race.  num_seqs == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             float scale, int32_t num_kv_heads,
+                             int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                             const pkv_cache_desc* cache, int32_t partition_tokens,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes paged_attn_decode needs for these arguments (0 when every
+ * sequence fits one partition).  (size_t)-1 for invalid arguments. */
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                        int32_t max_blocks_per_seq, int32_t partition_tokens,
+                                        const pkv_cache_desc* cache);
+
+/* Partition length in tokens that paged_attn_decode uses for these arguments
+ * (resolves partition_tokens == 0).  -1 for invalid arguments. */
+int32_t paged_attn_decode_partition_tokens(int32_t num_seqs, int32_t num_heads,
+                                           int32_t max_blocks_per_seq, int32_t partition_tokens,
+                                           const pkv_cache_desc* cache);
+
+/* ---------------------------------------------------------------------------
+ * reshape_and_cache — the slot-mapped cache write: for every token i with
+ * slot_mapping[i] >= 0, the K and V rows of every KV head are written to block
+ * slot / 16, offset slot % 16 ([blog] item 2: blocks are filled as tokens
+ * arrive; the slot encoding block * 16 + offset is this library's convention).
+ *
+ *   k, v          [num_tokens, num_kv_heads, 128] cache dtype, contiguous
+ *   slot_mapping  int32 [num_tokens]; negative = padding, skipped; slots must be
+ *                 unique (two tokens writing one slot race)
+ * Bit-exact copy of the input bits.  num_tokens == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+pkv_status reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                             const int32_t* slot_mapping, int32_t num_tokens,
+                             const pkv_cache_desc* cache, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * copy_blocks — the copy-on-write block copy ([blog] item 2: a block shared
+ * by parallel samples is copied before one of them writes to it).  For every
+ * pair (src, dst) the whole block — all 16 slots of every KV head, K and V —
+ * of src is copied to dst.
+ *
+ *   block_pairs   int32 [num_pairs, 2] row-major (src, dst); every dst distinct
+ *                 and no dst equal to any src (else the copies race)
+ * Bit-exact.  num_pairs == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+pkv_status copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
+                       const pkv_cache_desc* cache, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * gather_cache — inspection helper: paged K/V of each sequence copied to a
+ * contiguous [tokens, num_kv_heads, 128] array in logical token order.
+ * Sequence s occupies rows out_offsets[s] .. out_offsets[s] + context_lens[s].
+ *   out_offsets   int32 [num_seqs] (device)
+ * Bit-exact.
+ * ------------------------------------------------------------------------- */
+pkv_status gather_cache(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t max_blocks_per_seq, const int32_t* out_offsets,
+                        const pkv_cache_desc* cache, void* stream);
+
+const char* pkv_status_string(pkv_status s);
+const char* pkv_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Host block manager ([blog] item 2; [stack] "把显存当虚拟内存管").  Pure host
+ * code; no GPU needed.  Sequences are identified by caller-chosen int32 ids.
+ *
+ *   - the free list starts as free_order (a permutation of 0..num_blocks-1;
+ *     NULL = 0,1,2,...) and blocks are taken from its front; freed blocks are
+ *     appended to its back in block-table order;
+ *   - add: a new sequence with num_tokens tokens takes ceil(num_tokens/16)
+ *     blocks (ref = 1) and writes their slots (block*16 + offset) to slots_out
+ *     (host, may be NULL);
+ *   - fork: child shares every block of parent (ref += 1 each);
+ *   - append_slot: room for one more token.  At a block boundary a fresh block
+ *     is taken; otherwise if the last block is shared (ref > 1) a fresh block
+ *     replaces it in this sequence's table, the pair (old, new) is reported for
+ *     copy_blocks and the old block's ref drops by one (so the last sharer to
+ *     append writes in place);
+ *   - step: append_slot for each listed sequence in order, all or nothing;
+ *   - free: ref -= 1 for each block; blocks reaching 0 return to the free list.
+ * Every call either succeeds completely or returns an error without changing
+ * state (PKV_ERR_OUT_OF_BLOCKS when the free list is short, PKV_ERR_INVALID
+ * for unknown/duplicate ids or bad sizes).
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* free_order: host int32 [num_blocks] or NULL.  Returns NULL on bad arguments. */
+pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+pkv_status pkv_bm_add(pkv_block_manager* bm, int32_t seq, int32_t num_tokens, int32_t* slots_out);
+pkv_status pkv_bm_fork(pkv_block_manager* bm, int32_t parent, int32_t child);
+/* slot_out: host int32; cow_pair_out: host int32[2], (-1, -1) when no copy. */
+pkv_status pkv_bm_append_slot(pkv_block_manager* bm, int32_t seq, int32_t* slot_out, int32_t* cow_pair_out);
+/* slot_mapping_out: host int32 [n]; pairs_out: host int32 [n][2] capacity;
+ * num_pairs_out: host int32. */
+pkv_status pkv_bm_step(pkv_block_manager* bm, const int32_t* seqs, int32_t n,
+                       int32_t* slot_mapping_out, int32_t* pairs_out, int32_t* num_pairs_out);
+pkv_status pkv_bm_free(pkv_block_manager* bm, int32_t seq);
+/* table_out: host int32 [n][max_blocks], -1 padded; context_lens_out: host
+ * int32 [n] or NULL.  PKV_ERR_INVALID if a sequence has more than max_blocks. */
+pkv_status pkv_bm_block_table(const pkv_block_manager* bm, const int32_t* seqs, int32_t n,
+                              int32_t max_blocks, int32_t* table_out, int32_t* context_lens_out);
+int32_t pkv_bm_num_free(const pkv_block_manager* bm);
+int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);   /* -1 if out of range */
+int32_t pkv_bm_length(const pkv_block_manager* bm, int32_t seq);       /* -1 if unknown */
+int32_t pkv_bm_num_seq_blocks(const pkv_block_manager* bm, int32_t seq); /* -1 if unknown */
+/* allocated-but-unused slots of one sequence (at most 15); -1 if unknown */
+int32_t pkv_bm_waste(const pkv_block_manager* bm, int32_t seq);
+/* free list contents front to back: host int32 [capacity]; returns the count */
+int32_t pkv_bm_free_list(const pkv_block_manager* bm, int32_t* out, int32_t capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -32,11 +32,18 @@ class OracleStep:
 
 
 def run_decode_step(wl, *, max_blocks: Optional[int] = None, compute_out: bool = True,
-                    keep_before: bool = False, seqs: Optional[Sequence[int]] = None) -> OracleStep:
+                    keep_before: bool = False, seqs: Optional[Sequence[int]] = None,
+                    initial_cache=None) -> OracleStep:
+    """initial_cache: optional (K, V) [NB, 16, Hkv, 128] starting contents
+    (e.g. garbage in never-written slots); copied, not modified."""
     hkv = wl.num_kv_heads
     npdt = {"fp16": np.float16, "bf16": np.uint16}[wl.dtype]
     bm = BlockManager(wl.pool_blocks, BLOCK_SIZE, wl.free_order)
-    kc, vc = new_cache(wl.pool_blocks, BLOCK_SIZE, hkv, 128, npdt)
+    if initial_cache is None:
+        kc, vc = new_cache(wl.pool_blocks, BLOCK_SIZE, hkv, 128, npdt)
+    else:
+        kc = np.array(initial_cache[0], dtype=npdt, copy=True)
+        vc = np.array(initial_cache[1], dtype=npdt, copy=True)
     slot_mapping = pairs = None
     kb = vb = None
     for op in wl.ops:

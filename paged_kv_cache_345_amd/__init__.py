@@ -1,0 +1,397 @@
+"""Paged decode attention for MI355X (gfx950): Python binding of libpagedkv.so.
+
+Thin ctypes wrappers with the names of the C ABI in ``include/pagedkv.h``.
+They only marshal arguments — tensor pointers, shapes and the current HIP
+stream — and every step of the computation runs in the library's kernels.
+There is no fallback: if the library is not built or a tensor is not on the
+GPU, the call raises.
+
+Tensors (PyTorch is used for device memory and streams only):
+  q, out          [num_seqs, num_heads, 128]          float16 / bfloat16, GPU
+  k_cache, v_cache [num_blocks, num_kv_heads, 2048]   same dtype, GPU; the page
+                   layout inside the last dimension is the library's own (see
+                   pagedkv.h); use ``gather_cache`` or ``k_index``/``v_index`` to
+                   read it
+  block_tables    int32 [num_seqs, max_blocks_per_seq], GPU
+  context_lens    int32 [num_seqs], GPU
+  slot_mapping    int32 [num_tokens], GPU
+  block_pairs     int32 [num_pairs, 2], GPU
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+BLOCK_SIZE = 16
+HEAD_SIZE = 128
+PAGE_ELEMS = BLOCK_SIZE * HEAD_SIZE
+
+PKV_OK = 0
+PKV_ERR_INVALID = 1
+PKV_ERR_UNSUPPORTED = 2
+PKV_ERR_DEVICE = 3
+PKV_ERR_OUT_OF_BLOCKS = 4
+PKV_F16 = 0
+PKV_BF16 = 1
+
+# Every symbol pagedkv.h declares, with (restype, argtypes).
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_fl = ctypes.c_float
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", _i32), ("block_size", _i32), ("num_kv_heads", _i32),
+                ("head_size", _i32), ("dtype", _i32)]
+
+
+_DP = ctypes.POINTER(CacheDesc)
+
+SIGNATURES = {
+    "pkv_cache_bytes": (_sz, [_DP]),
+    "pkv_k_index": (_i64, [_DP, _i32, _i32, _i32, _i32]),
+    "pkv_v_index": (_i64, [_DP, _i32, _i32, _i32, _i32]),
+    "paged_attn_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _i32,
+                                 _vp, _sz, _vp]),
+    "paged_attn_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _DP]),
+    "paged_attn_decode_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _DP]),
+    "reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _DP, _vp]),
+    "copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _DP, _vp]),
+    "gather_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _DP, _vp]),
+    "pkv_status_string": (ctypes.c_char_p, [_i32]),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_bm_create": (_vp, [_i32, _i32, _i32p]),
+    "pkv_bm_destroy": (None, [_vp]),
+    "pkv_bm_add": (_i32, [_vp, _i32, _i32, _i32p]),
+    "pkv_bm_fork": (_i32, [_vp, _i32, _i32]),
+    "pkv_bm_append_slot": (_i32, [_vp, _i32, _i32p, _i32p]),
+    "pkv_bm_step": (_i32, [_vp, _i32p, _i32, _i32p, _i32p, _i32p]),
+    "pkv_bm_free": (_i32, [_vp, _i32]),
+    "pkv_bm_block_table": (_i32, [_vp, _i32p, _i32, _i32, _i32p, _i32p]),
+    "pkv_bm_num_free": (_i32, [_vp]),
+    "pkv_bm_refcount": (_i32, [_vp, _i32]),
+    "pkv_bm_length": (_i32, [_vp, _i32]),
+    "pkv_bm_num_seq_blocks": (_i32, [_vp, _i32]),
+    "pkv_bm_waste": (_i32, [_vp, _i32]),
+    "pkv_bm_free_list": (_i32, [_vp, _i32p, _i32]),
+}
+
+_LIB = None
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class OutOfBlocks(PagedKVError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_cache_345_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().pkv_status_string(status).decode()
+
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status == PKV_ERR_OUT_OF_BLOCKS:
+        raise OutOfBlocks(status, what)
+    if status != PKV_OK:
+        raise PagedKVError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# tensors and streams
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return PKV_F16
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def _gpu(t, name: str, dtype=None, ndim: Optional[int] = None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def cache_desc(num_blocks: int, num_kv_heads: int, dtype) -> CacheDesc:
+    torch = _torch()
+    code = dtype if isinstance(dtype, int) else (PKV_F16 if dtype == torch.float16 else PKV_BF16)
+    return CacheDesc(int(num_blocks), BLOCK_SIZE, int(num_kv_heads), HEAD_SIZE, code)
+
+
+def _desc_of(k_cache) -> CacheDesc:
+    if k_cache.dim() != 3 or k_cache.shape[2] != PAGE_ELEMS:
+        raise ValueError(f"cache must be [num_blocks, num_kv_heads, {PAGE_ELEMS}], got {tuple(k_cache.shape)}")
+    return CacheDesc(int(k_cache.shape[0]), BLOCK_SIZE, int(k_cache.shape[1]), HEAD_SIZE, _dtype_code(k_cache))
+
+
+def allocate_cache(num_blocks: int, num_kv_heads: int, dtype, device="cuda") -> Tuple[object, object]:
+    """Uninitialised K and V caches of pkv_cache_bytes() each."""
+    torch = _torch()
+    desc = cache_desc(num_blocks, num_kv_heads, dtype)
+    nbytes = lib().pkv_cache_bytes(ctypes.byref(desc))
+    if nbytes == 0:
+        raise ValueError("invalid cache shape")
+    shape = (num_blocks, num_kv_heads, PAGE_ELEMS)
+    return (torch.empty(shape, dtype=dtype, device=device), torch.empty(shape, dtype=dtype, device=device))
+
+
+def k_index(desc: CacheDesc, block: int, head: int, token: int, dim: int) -> int:
+    return int(lib().pkv_k_index(ctypes.byref(desc), block, head, token, dim))
+
+
+def v_index(desc: CacheDesc, block: int, head: int, token: int, dim: int) -> int:
+    return int(lib().pkv_v_index(ctypes.byref(desc), block, head, token, dim))
+
+
+# ---------------------------------------------------------------------------
+# the hot path
+# ---------------------------------------------------------------------------
+
+def workspace_size(num_seqs: int, num_heads: int, max_blocks_per_seq: int, desc: CacheDesc,
+                   partition_tokens: int = 0) -> int:
+    n = lib().paged_attn_decode_workspace_size(num_seqs, num_heads, max_blocks_per_seq, partition_tokens,
+                                               ctypes.byref(desc))
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedKVError(PKV_ERR_INVALID, "paged_attn_decode_workspace_size")
+    return int(n)
+
+
+def partition_tokens_for(num_seqs: int, num_heads: int, max_blocks_per_seq: int, desc: CacheDesc,
+                         partition_tokens: int = 0) -> int:
+    n = lib().paged_attn_decode_partition_tokens(num_seqs, num_heads, max_blocks_per_seq, partition_tokens,
+                                                 ctypes.byref(desc))
+    if n < 0:
+        raise PagedKVError(PKV_ERR_INVALID, "paged_attn_decode_partition_tokens")
+    return int(n)
+
+
+def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                      num_kv_heads: int, *, partition_tokens: int = 0, workspace=None, stream=None):
+    """out[s, h] = softmax(scale * q[s, h] . K[s, :ctx, h // g]) V[s, :ctx, h // g]."""
+    torch = _torch()
+    desc = _desc_of(k_cache)
+    if desc.num_kv_heads != num_kv_heads:
+        raise ValueError("num_kv_heads does not match the cache")
+    num_seqs, num_heads, hs = q.shape
+    if hs != HEAD_SIZE or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must be [num_seqs, num_heads, 128]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    mbps = int(block_tables.shape[1])
+    ptrs = [_gpu(out, "out", q.dtype, 3), _gpu(q, "q", None, 3), _gpu(k_cache, "k_cache", q.dtype),
+            _gpu(v_cache, "v_cache", q.dtype), _gpu(block_tables, "block_tables", torch.int32, 2),
+            _gpu(context_lens, "context_lens", torch.int32, 1)]
+    if context_lens.shape[0] != num_seqs or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("context_lens / v_cache shape mismatch")
+    need = workspace_size(num_seqs, num_heads, mbps, desc, partition_tokens) if num_seqs else 0
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = _gpu(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().paged_attn_decode(*ptrs, float(scale), int(num_kv_heads), int(num_seqs), int(num_heads), mbps,
+                                 ctypes.byref(desc), int(partition_tokens), ws_ptr, ws_bytes,
+                                 _stream_handle(stream))
+    _check(st, "paged_attn_decode")
+    return out
+
+
+def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, stream=None):
+    """Write k[i], v[i] ([num_kv_heads, 128]) of every token i to slot_mapping[i]."""
+    torch = _torch()
+    desc = _desc_of(k_cache)
+    n = int(slot_mapping.shape[0])
+    if tuple(k.shape) != (n, desc.num_kv_heads, HEAD_SIZE) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k, v must be [num_tokens, num_kv_heads, 128]")
+    st = lib().reshape_and_cache(_gpu(k, "k", k_cache.dtype), _gpu(v, "v", k_cache.dtype),
+                                 _gpu(k_cache, "k_cache"), _gpu(v_cache, "v_cache", k_cache.dtype),
+                                 _gpu(slot_mapping, "slot_mapping", torch.int32, 1), n, ctypes.byref(desc),
+                                 _stream_handle(stream))
+    _check(st, "reshape_and_cache")
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
+    """Copy every (src, dst) block of block_pairs, K and V, all heads."""
+    torch = _torch()
+    desc = _desc_of(k_cache)
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [num_pairs, 2]")
+    n = int(block_pairs.shape[0])
+    if n == 0:
+        return
+    st = lib().copy_blocks(_gpu(k_cache, "k_cache"), _gpu(v_cache, "v_cache", k_cache.dtype),
+                           _gpu(block_pairs, "block_pairs", torch.int32, 2), n, ctypes.byref(desc),
+                           _stream_handle(stream))
+    _check(st, "copy_blocks")
+
+
+def gather_cache(k_out, v_out, k_cache, v_cache, block_tables, context_lens, out_offsets, *, stream=None):
+    """Paged K/V of every sequence into contiguous [tokens, num_kv_heads, 128]."""
+    torch = _torch()
+    desc = _desc_of(k_cache)
+    num_seqs, mbps = block_tables.shape
+    st = lib().gather_cache(_gpu(k_out, "k_out", k_cache.dtype), _gpu(v_out, "v_out", k_cache.dtype),
+                            _gpu(k_cache, "k_cache"), _gpu(v_cache, "v_cache", k_cache.dtype),
+                            _gpu(block_tables, "block_tables", torch.int32, 2),
+                            _gpu(context_lens, "context_lens", torch.int32, 1), int(num_seqs), int(mbps),
+                            _gpu(out_offsets, "out_offsets", torch.int32, 1), ctypes.byref(desc),
+                            _stream_handle(stream))
+    _check(st, "gather_cache")
+
+
+# ---------------------------------------------------------------------------
+# host block manager (C++)
+# ---------------------------------------------------------------------------
+
+def _i32_array(values) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_i32p)
+
+
+class BlockManager:
+    """The library's host block manager (pkv_bm_*): free list, refcounts,
+    per-sequence block tables, copy-on-write on append."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE, free_order=None):
+        order = None if free_order is None else _i32_array(free_order)
+        if order is not None and order.shape[0] != num_blocks:
+            raise ValueError("free_order must have num_blocks entries")
+        self._order = order
+        h = lib().pkv_bm_create(int(num_blocks), int(block_size), None if order is None else _p(order))
+        if not h:
+            raise ValueError("pkv_bm_create rejected its arguments")
+        self._h = ctypes.c_void_p(h)
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _LIB is not None:
+            _LIB.pkv_bm_destroy(h)
+            self._h = None
+
+    def add(self, seq: int, num_tokens: int) -> np.ndarray:
+        slots = np.empty(max(int(num_tokens), 1), dtype=np.int32)
+        _check(lib().pkv_bm_add(self._h, int(seq), int(num_tokens), _p(slots)), "pkv_bm_add")
+        return slots[: int(num_tokens)]
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib().pkv_bm_fork(self._h, int(parent), int(child)), "pkv_bm_fork")
+
+    def append_slot(self, seq: int):
+        slot = np.zeros(1, dtype=np.int32)
+        pair = np.zeros(2, dtype=np.int32)
+        _check(lib().pkv_bm_append_slot(self._h, int(seq), _p(slot), _p(pair)), "pkv_bm_append_slot")
+        return int(slot[0]), (None if pair[0] < 0 else (int(pair[0]), int(pair[1])))
+
+    def step(self, seqs: Sequence[int]):
+        seqs_a = _i32_array(list(seqs))
+        n = int(seqs_a.shape[0])
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        npairs = np.zeros(1, dtype=np.int32)
+        _check(lib().pkv_bm_step(self._h, _p(seqs_a), n, _p(slots), _p(pairs), _p(npairs)), "pkv_bm_step")
+        return slots[:n].copy(), pairs[: int(npairs[0])].copy()
+
+    def free_seq(self, seq: int) -> None:
+        _check(lib().pkv_bm_free(self._h, int(seq)), "pkv_bm_free")
+
+    def block_table(self, seqs: Sequence[int], max_blocks: int) -> np.ndarray:
+        seqs_a = _i32_array(list(seqs))
+        n = int(seqs_a.shape[0])
+        table = np.empty((max(n, 1), max(int(max_blocks), 1)), dtype=np.int32)
+        _check(lib().pkv_bm_block_table(self._h, _p(seqs_a), n, int(max_blocks), _p(table), None),
+               "pkv_bm_block_table")
+        return table[:n, : int(max_blocks)].copy()
+
+    def context_lens(self, seqs: Sequence[int]) -> np.ndarray:
+        return np.asarray([self.length(s) for s in seqs], dtype=np.int32)
+
+    def num_free(self) -> int:
+        return int(lib().pkv_bm_num_free(self._h))
+
+    def num_used(self) -> int:
+        return self.num_blocks - self.num_free()
+
+    def refcount(self, block: int) -> int:
+        return int(lib().pkv_bm_refcount(self._h, int(block)))
+
+    def length(self, seq: int) -> int:
+        return int(lib().pkv_bm_length(self._h, int(seq)))
+
+    def num_seq_blocks(self, seq: int) -> int:
+        return int(lib().pkv_bm_num_seq_blocks(self._h, int(seq)))
+
+    def waste(self, seq: int) -> int:
+        return int(lib().pkv_bm_waste(self._h, int(seq)))
+
+    def free_list(self) -> np.ndarray:
+        n = self.num_free()
+        out = np.empty(max(n, 1), dtype=np.int32)
+        lib().pkv_bm_free_list(self._h, _p(out), n)
+        return out[:n].copy()
+
+
+__all__ = [
+    "LIB_PATH", "BLOCK_SIZE", "HEAD_SIZE", "PAGE_ELEMS", "CacheDesc", "PagedKVError", "OutOfBlocks",
+    "lib", "status_string", "version", "cache_desc", "allocate_cache", "k_index", "v_index",
+    "workspace_size", "partition_tokens_for", "paged_attn_decode", "reshape_and_cache", "copy_blocks",
+    "gather_cache", "BlockManager", "SIGNATURES",
+]

@@ -1,0 +1,139 @@
+// Cache data-movement kernels: slot-mapped write, copy-on-write block copy and
+// the paged -> contiguous inspection gather.  All of them move bits only.
+//
+// Slot model from page "vLLM 部署与 PagedAttention 原理 · 检索整理（CSDN 频道批次）",
+// item 2: tokens fill fixed-size blocks reached through a block table, and a
+// block shared by parallel samples is copied before it is written.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+// One thread per (token, KV head, 8-dim chunk): 16 threads cover a 256-byte
+// input row.  K lands as one 16-byte store (8 consecutive dims of one token are
+// contiguous in the K page); V lands as eight 2-byte stores (consecutive dims
+// of one token are 16 bytes apart in the V page).
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int64_t num_rows,
+    int num_kv_heads, int64_t num_slots) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = gid >> 4;  // token * Hkv + head
+  const int c = static_cast<int>(gid & 15);
+  if (row >= num_rows) return;
+  const int64_t token = row / num_kv_heads;
+  const int h = static_cast<int>(row - token * num_kv_heads);
+  const int32_t slot = slot_mapping[token];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t block = slot >> 4;
+  const int t = slot & 15;
+  const int64_t page = (block * num_kv_heads + h) * kPageElems;
+
+  const uint4 kv = reinterpret_cast<const uint4*>(k + row * kHeadSize)[c];
+  *reinterpret_cast<uint4*>(k_cache + page + k_page_offset(t, 8 * c)) = kv;
+
+  const uint4 vv = reinterpret_cast<const uint4*>(v + row * kHeadSize)[c];
+  uint16_t* vp = v_cache + page;
+  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint16_t bits = static_cast<uint16_t>((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+    vp[v_page_offset(t, 8 * c + e)] = bits;
+  }
+}
+
+// One work-group of 256 threads copies one 4 KiB page (16 bytes per thread).
+// Work-group index -> (pair, which of the 2*Hkv pages of the block).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ block_pairs, int num_kv_heads,
+                                                          int32_t num_blocks) {
+  const int64_t wg = blockIdx.x;
+  const int pages = 2 * num_kv_heads;
+  const int64_t pair = wg / pages;
+  const int page = static_cast<int>(wg - pair * pages);
+  const int32_t src = block_pairs[2 * pair];
+  const int32_t dst = block_pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint16_t* base = page < num_kv_heads ? k_cache : v_cache;
+  const int h = page < num_kv_heads ? page : page - num_kv_heads;
+  const uint4* s = reinterpret_cast<const uint4*>(base + (static_cast<int64_t>(src) * num_kv_heads + h) * kPageElems);
+  uint4* d = reinterpret_cast<uint4*>(base + (static_cast<int64_t>(dst) * num_kv_heads + h) * kPageElems);
+  d[threadIdx.x] = s[threadIdx.x];
+}
+
+// One work-group per (sequence, logical block).  Thread -> (token, head, chunk).
+__global__ __launch_bounds__(256) void gather_cache_kernel(
+    uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ out_offsets, int max_blocks_per_seq,
+    int num_kv_heads, int32_t num_blocks) {
+  const int64_t wg = blockIdx.x;
+  const int64_t s = wg / max_blocks_per_seq;
+  const int j = static_cast<int>(wg - s * max_blocks_per_seq);
+  int64_t L = context_lens[s];
+  if (L > static_cast<int64_t>(max_blocks_per_seq) * kBlockSize) L = static_cast<int64_t>(max_blocks_per_seq) * kBlockSize;
+  const int64_t first = static_cast<int64_t>(j) * kBlockSize;
+  if (first >= L) return;
+  const int32_t block = block_tables[s * max_blocks_per_seq + j];
+  if (block < 0 || block >= num_blocks) return;
+  const int ntok = static_cast<int>(L - first < kBlockSize ? L - first : kBlockSize);
+  const int64_t row0 = static_cast<int64_t>(out_offsets[s]) + first;
+  const int work = kBlockSize * num_kv_heads * 16;
+  for (int idx = threadIdx.x; idx < work; idx += blockDim.x) {
+    const int c = idx & 15;
+    const int t = (idx >> 4) & 15;
+    const int h = idx >> 8;
+    if (t >= ntok) continue;
+    const int64_t page = (static_cast<int64_t>(block) * num_kv_heads + h) * kPageElems;
+    const int64_t out_row = (row0 + t) * num_kv_heads + h;
+    reinterpret_cast<uint4*>(k_out + out_row * kHeadSize)[c] =
+        *reinterpret_cast<const uint4*>(k_cache + page + k_page_offset(t, 8 * c));
+    uint16_t e16[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) e16[e] = v_cache[page + v_page_offset(t, 8 * c + e)];
+    uint4 packed;
+    packed.x = e16[0] | (static_cast<uint32_t>(e16[1]) << 16);
+    packed.y = e16[2] | (static_cast<uint32_t>(e16[3]) << 16);
+    packed.z = e16[4] | (static_cast<uint32_t>(e16[5]) << 16);
+    packed.w = e16[6] | (static_cast<uint32_t>(e16[7]) << 16);
+    reinterpret_cast<uint4*>(v_out + out_row * kHeadSize)[c] = packed;
+  }
+}
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                    int32_t num_blocks, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(num_tokens) * num_kv_heads;
+  const int64_t threads = rows * 16;
+  const int64_t grid = (threads + 255) / 256;
+  reshape_and_cache_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(k_cache),
+      static_cast<uint16_t*>(v_cache), slot_mapping, rows, num_kv_heads, static_cast<int64_t>(num_blocks) * kBlockSize);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
+                              int32_t num_kv_heads, int32_t num_blocks, hipStream_t stream) {
+  const int64_t grid = static_cast<int64_t>(num_pairs) * 2 * num_kv_heads;
+  copy_blocks_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(
+      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_pairs, num_kv_heads, num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_cache(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, const int32_t* out_offsets, int32_t num_kv_heads,
+                               int32_t num_blocks, hipStream_t stream) {
+  const int64_t grid = static_cast<int64_t>(num_seqs) * max_blocks_per_seq;
+  gather_cache_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(
+      static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out), static_cast<const uint16_t*>(k_cache),
+      static_cast<const uint16_t*>(v_cache), block_tables, context_lens, out_offsets, max_blocks_per_seq,
+      num_kv_heads, num_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,160 @@
+// Device-side definitions shared by the gfx950 kernels of libpagedkv.
+//
+// Page layout (one page = one (block, KV head) = 16 tokens x 128 dims, 2048
+// two-byte elements; a block of 16 tokens of one head holds 2048 elements as on
+// page "vLLM 深度解析：以 PagedAttention 与内核生态构建高吞吐 LLM 推理引擎", §2.1).
+// The element order inside a page is this library's own, chosen so that a
+// 64-lane wave reads a page as four contiguous 1 KiB loads of 16 bytes per lane
+// and each lane's 16 bytes are directly a matrix-core operand fragment:
+//
+//   K: offset(t, d) = (d/8)*128 + t*8 + d%8
+//      load i, lane l -> token l%16, dims 8*(4i + l/16) .. +8
+//      (the A operand of v_mfma_f32_16x16x32_{f16,bf16} with rows = tokens)
+//   V: offset(t, d) = ((d/16)/2)*512 + (16*(t/4) + d%16)*8 + ((d/16)%2)*4 + t%4
+//      load p, lane l, element e -> token 4*(l/16) + e%4, dim 16*(2p + e/4) + l%16
+//      (two B operands of v_mfma_f32_16x16x16_{f16,bf16}, k = tokens)
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlockSize = 16;
+constexpr int kHeadSize = 128;
+constexpr int kPageElems = kBlockSize * kHeadSize;  // 2048
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;                   // decode work-groups: 4 independent waves
+constexpr int kMaxPartitions = 4096;                // reduce kernel LDS bound
+constexpr int kMaxBlocksPerPartition = 64;          // one block id per lane
+constexpr float kMaskedLogit = -__builtin_inff();
+constexpr float kInitMax = -1.0e30f;                // finite: exp2(kInitMax - kInitMax) == 1
+
+__host__ __device__ inline int k_page_offset(int t, int d) { return (d >> 3) * 128 + t * 8 + (d & 7); }
+
+__host__ __device__ inline int v_page_offset(int t, int d) {
+  const int j = d >> 4, c = d & 15, grp = t >> 2, i = t & 3;
+  return (j >> 1) * 512 + (16 * grp + c) * 8 + (j & 1) * 4 + i;
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Element-type traits.  Storage is 16-bit words; arithmetic is fp32.
+// ---------------------------------------------------------------------------
+struct F16 {
+  __device__ static inline float lo(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[0]; }
+  __device__ static inline float hi(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[1]; }
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+  }
+  __device__ static inline uint16_t from_f32(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+  __device__ static inline float round(float x) { return (float)(_Float16)x; }
+  __device__ static inline uint32_t pack2(float a, float b) {
+    half2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  __device__ static inline float4_t mfma_qk(uint4 a, uint4 b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
+  }
+  __device__ static inline float4_t mfma_pv(uint2 a, uint2 b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a), __builtin_bit_cast(half4_t, b), c,
+                                                 0, 0, 0);
+  }
+};
+
+struct BF16 {
+  __device__ static inline float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static inline float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a), __builtin_bit_cast(bf162_t, b), c, false);
+  }
+  __device__ static inline uint16_t from_f32(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+  __device__ static inline float round(float x) { return (float)(__bf16)x; }
+  __device__ static inline uint32_t pack2(float a, float b) {
+    bf162_t h = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  __device__ static inline float4_t mfma_qk(uint4 a, uint4 b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, a), __builtin_bit_cast(bf168_t, b), c,
+                                                   0, 0, 0);
+  }
+  __device__ static inline float4_t mfma_pv(uint2 a, uint2 b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a), __builtin_bit_cast(short4_t, b),
+                                                     c, 0, 0, 0);
+  }
+};
+
+template <class DT>
+__device__ inline float dot8(uint4 a, uint4 b, float c) {
+  c = DT::dot2(a.x, b.x, c);
+  c = DT::dot2(a.y, b.y, c);
+  c = DT::dot2(a.z, b.z, c);
+  c = DT::dot2(a.w, b.w, c);
+  return c;
+}
+
+// element e (0..7) of an 8 x 16-bit vector held in a uint4, as fp32
+template <class DT>
+__device__ inline float elem(const uint4& v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (e & 1) ? DT::hi(w) : DT::lo(w);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (wave64).
+// ---------------------------------------------------------------------------
+template <int kCtrl>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// max / sum over the 16 lanes of each row, result in every lane of the row
+__device__ inline float row_max16(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return x;
+}
+__device__ inline float row_sum16(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppRowMirror>(x);
+  return x;
+}
+
+__device__ inline float lane_from(float x, int src_lane) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
+}
+
+// sum / max over the 4 rows (lanes l, l^16, l^32, l^48), result in every lane
+__device__ inline float cross_row_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+__device__ inline float cross_row_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline int wave_id_uniform() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+}  // namespace pkv
