@@ -28,8 +28,8 @@
  *   - Contents of device arrays (block ids, slots, context lengths) are the
  *     caller's contract and are not checked on the fast path.  Values outside
  *     the pool never cause an out-of-bounds access: a block id outside
- *     [0, num_blocks) is treated as an all-masked block and an out-of-range
- *     slot or block pair is skipped.
+ *     [0, num_blocks) is read from block 0 instead (that sequence's output is
+ *     then unspecified) and an out-of-range slot or block pair is skipped.
  *
  * KV page layout (element offsets; one element = 2 bytes).  k_cache and v_cache
  * are separate buffers of pkv_cache_bytes() each.  Page (b, h) — block b, KV

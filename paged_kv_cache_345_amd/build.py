@@ -25,7 +25,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.hip", "decode.hip", "cache_ops.hip", "block_manager.cpp"]
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+COMMON = ["-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-fgpu-flush-denormals-to-zero", "-munsafe-fp-atomics"]
 

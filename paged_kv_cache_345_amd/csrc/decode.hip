@@ -39,6 +39,36 @@ __device__ inline int clamped_len(const DecodeArgs& a, int s) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
+// Work-group -> work items, XCD-aware.  Work-groups are dispatched to the 8
+// XCDs round-robin (XCD = blockIdx.x % 8), each XCD with its own L2.  The
+// logical work space is ordered (head [x tile], partition, group of 4
+// consecutive sequences) and cut into 8 contiguous chunks, one per XCD: each
+// XCD walks a few heads, partition by partition, through the sequences in
+// order, and the 4 waves of a work-group take 4 consecutive sequences.
+// Sequences that share prompt blocks (parallel samples, numbered
+// consecutively) thus read the same pages on the same CU and L2 at about the
+// same time.  Returns false for padding work-groups and missing sequences.
+__device__ inline bool xcd_item(const DecodeArgs& a, int heads, int& s, int& h, int& p) {
+  const int64_t n_sb = (a.num_seqs + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t total = static_cast<int64_t>(heads) * a.parts_max * n_sb;
+  const int64_t per_xcd = (total + kNumXcd - 1) / kNumXcd;
+  const int64_t w = blockIdx.x;
+  const int64_t lam = (w % kNumXcd) * per_xcd + w / kNumXcd;
+  if (lam >= total) return false;
+  const int64_t sb = lam % n_sb;
+  const int64_t rest = lam / n_sb;
+  p = static_cast<int>(rest % a.parts_max);
+  h = static_cast<int>(rest / a.parts_max);
+  s = static_cast<int>(sb * kWavesPerGroup) + wave_id_uniform();
+  return s < a.num_seqs;
+}
+
+__host__ inline int64_t xcd_grid(int64_t heads, int64_t parts, int64_t num_seqs) {
+  const int64_t n_sb = (num_seqs + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t total = heads * parts * n_sb;
+  return ((total + kNumXcd - 1) / kNumXcd) * kNumXcd;
+}
+
 // Masks that zero the 16-bit elements of a V fragment whose token is not
 // valid.  Word k of a lane's 16-byte V fragment holds tokens 4G + (2k & 3) and
 // 4G + (2k+1 & 3), so words x,z share one mask and y,w the other.
@@ -55,29 +85,32 @@ __device__ inline void mask_v(uint4 (&vv)[4], int grp, int nvalid) {
   }
 }
 
-__device__ inline void load_page(uint4 (&kv)[4], uint4 (&vv)[4], const uint16_t* kp, const uint16_t* vp, int lane) {
-  const uint4* k4 = reinterpret_cast<const uint4*>(kp) + lane;
-  const uint4* v4 = reinterpret_cast<const uint4*>(vp) + lane;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) kv[i] = k4[64 * i];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) vv[i] = v4[64 * i];
+// Four contiguous 1 KiB wave loads per K page and per V page, as raw buffer
+// loads: one buffer descriptor per page (wave-uniform, scalar registers, with a
+// 4 KiB record limit) and a single per-lane byte offset shared by K and V.
+__device__ inline void load_page(uint4 (&kv)[4], uint4 (&vv)[4], const uint16_t* kp, const uint16_t* vp,
+                                 uint32_t lane_bytes) {
+  const __amdgpu_buffer_rsrc_t kr = page_rsrc(kp);
+  const __amdgpu_buffer_rsrc_t vr = page_rsrc(vp);
+  kv[0] = load16<0>(kr, lane_bytes);
+  kv[1] = load16<1024>(kr, lane_bytes);
+  kv[2] = load16<2048>(kr, lane_bytes);
+  kv[3] = load16<3072>(kr, lane_bytes);
+  vv[0] = load16<0>(vr, lane_bytes);
+  vv[1] = load16<1024>(vr, lane_bytes);
+  vv[2] = load16<2048>(vr, lane_bytes);
+  vv[3] = load16<3072>(vr, lane_bytes);
 }
 
 // ---------------------------------------------------------------------------
 // MHA: one query head per KV head.
 // ---------------------------------------------------------------------------
 template <class DT>
-__global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 4) void decode_mha_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave_id_uniform();
   const int H = a.num_kv_heads;
-  const int64_t n_items = static_cast<int64_t>(a.parts_max) * a.num_seqs * H;
-  if (item >= n_items) return;
-  const int h = static_cast<int>(item % H);
-  const int64_t rest = item / H;
-  const int s = static_cast<int>(rest % a.num_seqs);
-  const int p = static_cast<int>(rest / a.num_seqs);
+  int s, h, p;
+  if (!xcd_item(a, H, s, h, p)) return;
 
   const int L = clamped_len(a, s);
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
@@ -114,17 +147,17 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 
   // One block of this partition: QK, online softmax, V accumulation.
-  auto process = [&](uint4 (&kv)[4], uint4 (&vv)[4], int jj) __attribute__((always_inline)) {
-    const int bid = __builtin_amdgcn_readlane(my_bid, jj);
-    const bool bad = static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks);
-    const int nvalid = bad ? 0 : min(kBlockSize, L - (j0 + jj) * kBlockSize);
+  // kTail: the sequence's last block, which may hold fewer than 16 tokens;
+  // every other block is full and needs no masking.
+  auto process = [&]<bool kTail>(uint4 (&kv)[4], uint4 (&vv)[4], int jj) __attribute__((always_inline)) {
+    const int nvalid = kTail ? min(kBlockSize, L - (j0 + jj) * kBlockSize) : kBlockSize;
 
     // QK: lane (grp, col) holds 32 of token col's 128 dims
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) part = dot8<DT>(qf[i], kv[i], part);
     part = cross_row_sum(part);
-    const float x = col < nvalid ? part * a.scale_log2e : kMaskedLogit;
+    const float x = (!kTail || col < nvalid) ? part * a.scale_log2e : kMaskedLogit;
 
     // online softmax with a wave-uniform running max
     const float m_new = fmaxf(m, row_max16(x));
@@ -136,7 +169,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
     float wi[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) wi[i] = lane_from(w, src_row_lane + i);
-    if (nvalid < kBlockSize) mask_v(vv, grp, nvalid);
+    if (kTail && nvalid < kBlockSize) mask_v(vv, grp, nvalid);
 
     // V: lane (grp, col) holds tokens 4grp..4grp+3 of dims 16j + col, j = 0..7
 #pragma unroll
@@ -155,26 +188,27 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
     const int bid = __builtin_amdgcn_readlane(my_bid, jj);
     const bool bad = static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks);
     const int64_t off = static_cast<int64_t>(bad ? 0 : bid) * page_stride + head_off;
-    load_page(kv, vv, a.k_cache + off, a.v_cache + off, lane);
+    load_page(kv, vv, a.k_cache + off, a.v_cache + off, static_cast<uint32_t>(lane) * 16u);
   };
 
   // two register sets: one block in flight while the other is consumed
   uint4 ka[4], va[4], kb[4], vb[4];
   issue(ka, va, 0);
   int jj = 0;
-  // steady state: no conditional loads, so each wait leaves the other set in flight
+  // steady state: full blocks only and no conditional loads, so each wait
+  // leaves the other register set in flight
   for (; jj + 2 < nb; jj += 2) {
     issue(kb, vb, jj + 1);
-    process(ka, va, jj);
+    process.template operator()<false>(ka, va, jj);
     issue(ka, va, jj + 2);
-    process(kb, vb, jj + 1);
+    process.template operator()<false>(kb, vb, jj + 1);
   }
   if (jj + 1 < nb) {
     issue(kb, vb, jj + 1);
-    process(ka, va, jj);
-    process(kb, vb, jj + 1);
+    process.template operator()<false>(ka, va, jj);
+    process.template operator()<true>(kb, vb, jj + 1);
   } else {
-    process(ka, va, jj);
+    process.template operator()<true>(ka, va, jj);
   }
 
   z = row_sum16(z);
@@ -206,16 +240,11 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
 template <class DT>
 __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave_id_uniform();
   const int Hkv = a.num_kv_heads;
-  const int64_t n_items = static_cast<int64_t>(a.parts_max) * a.num_seqs * Hkv * a.head_tiles;
-  if (item >= n_items) return;
-  const int tile = static_cast<int>(item % a.head_tiles);
-  int64_t rest = item / a.head_tiles;
-  const int kvh = static_cast<int>(rest % Hkv);
-  rest /= Hkv;
-  const int s = static_cast<int>(rest % a.num_seqs);
-  const int p = static_cast<int>(rest / a.num_seqs);
+  int s, ht, p;
+  if (!xcd_item(a, Hkv * a.head_tiles, s, ht, p)) return;
+  const int kvh = ht / a.head_tiles;
+  const int tile = ht - kvh * a.head_tiles;
 
   const int h0 = kvh * a.group + tile * 16;
   const int nh = min(16, a.group - tile * 16);
@@ -259,10 +288,8 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) O[j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](uint4 (&kv)[4], uint4 (&vv)[4], int jj) __attribute__((always_inline)) {
-    const int bid = __builtin_amdgcn_readlane(my_bid, jj);
-    const bool bad = static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks);
-    const int nvalid = bad ? 0 : min(kBlockSize, L - (j0 + jj) * kBlockSize);
+  auto process = [&]<bool kTail>(uint4 (&kv)[4], uint4 (&vv)[4], int jj) __attribute__((always_inline)) {
+    const int nvalid = kTail ? min(kBlockSize, L - (j0 + jj) * kBlockSize) : kBlockSize;
 
     // S[token 4grp + r][head col]
     float4_t S = {0.f, 0.f, 0.f, 0.f};
@@ -270,7 +297,8 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) S = DT::mfma_qk(kv[i], qf[i], S);
     float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = (4 * grp + r < nvalid) ? S[r] * a.scale_log2e : kMaskedLogit;
+    for (int r = 0; r < 4; ++r)
+      x[r] = (!kTail || 4 * grp + r < nvalid) ? S[r] * a.scale_log2e : kMaskedLogit;
 
     float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     bm = cross_row_max(bm);
@@ -298,7 +326,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     uint2 pa;
     pa.x = DT::pack2(pr[0], pr[1]);
     pa.y = DT::pack2(pr[2], pr[3]);
-    if (nvalid < kBlockSize) mask_v(vv, grp, nvalid);
+    if (kTail && nvalid < kBlockSize) mask_v(vv, grp, nvalid);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint4& f = vv[j >> 1];
@@ -310,25 +338,26 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     const int bid = __builtin_amdgcn_readlane(my_bid, jj);
     const bool bad = static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks);
     const int64_t off = static_cast<int64_t>(bad ? 0 : bid) * page_stride + head_off;
-    load_page(kv, vv, a.k_cache + off, a.v_cache + off, lane);
+    load_page(kv, vv, a.k_cache + off, a.v_cache + off, static_cast<uint32_t>(lane) * 16u);
   };
 
   uint4 ka[4], va[4], kb[4], vb[4];
   issue(ka, va, 0);
   int jj = 0;
-  // steady state: no conditional loads, so each wait leaves the other set in flight
+  // steady state: full blocks only and no conditional loads, so each wait
+  // leaves the other register set in flight
   for (; jj + 2 < nb; jj += 2) {
     issue(kb, vb, jj + 1);
-    process(ka, va, jj);
+    process.template operator()<false>(ka, va, jj);
     issue(ka, va, jj + 2);
-    process(kb, vb, jj + 1);
+    process.template operator()<false>(kb, vb, jj + 1);
   }
   if (jj + 1 < nb) {
     issue(kb, vb, jj + 1);
-    process(ka, va, jj);
-    process(kb, vb, jj + 1);
+    process.template operator()<false>(ka, va, jj);
+    process.template operator()<true>(kb, vb, jj + 1);
   } else {
-    process(ka, va, jj);
+    process.template operator()<true>(ka, va, jj);
   }
 
   const float Z = cross_row_sum(z);  // head col's total
@@ -435,9 +464,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 
 template <class DT>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t items_per_part = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * (a.group == 1 ? 1 : a.head_tiles);
-  const int64_t items = items_per_part * a.parts_max;
-  const int64_t grid = (items + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t heads = static_cast<int64_t>(a.num_kv_heads) * (a.group == 1 ? 1 : a.head_tiles);
+  const int64_t grid = xcd_grid(heads, a.parts_max, a.num_seqs);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (a.group == 1)
     decode_mha_kernel<DT><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);

@@ -26,6 +26,7 @@ constexpr int kHeadSize = 128;
 constexpr int kPageElems = kBlockSize * kHeadSize;  // 2048
 constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 4;                   // decode work-groups: 4 independent waves
+constexpr int kNumXcd = 8;                          // MI355X: 8 XCDs, work-groups dealt round-robin
 constexpr int kMaxPartitions = 4096;                // reduce kernel LDS bound
 constexpr int kMaxBlocksPerPartition = 64;          // one block id per lane
 constexpr float kMaskedLogit = -__builtin_inff();
@@ -151,6 +152,21 @@ __device__ inline float cross_row_max(float x) {
   x = fmaxf(x, __shfl_xor(x, 16, 64));
   x = fmaxf(x, __shfl_xor(x, 32, 64));
   return x;
+}
+
+// Buffer descriptor covering one 4 KiB page (gfx9 descriptor word 3:
+// 32-bit data format, no swizzle); reads past the page return 0.
+constexpr int kBufferDword3 = 0x00020000;
+__device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* page) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(page), 0, kPageElems * 2, kBufferDword3);
+}
+typedef int int4_t __attribute__((ext_vector_type(4)));
+// 16 bytes at lane_off + kConstOff of the descriptor's range (the constant goes
+// to the instruction's immediate offset, the lane part to one VGPR)
+template <int kConstOff>
+__device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off) {
+  return __builtin_bit_cast(uint4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(lane_off), kConstOff, 0));
 }
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
