@@ -36,7 +36,11 @@ def log(msg: str) -> None:
 
 
 def step_bytes(wl, step):
-    """Algorithmic bytes of one step (see the design doc for the accounting)."""
+    """Algorithmic bytes of one step.  K/V: every unique live (block, slot) once,
+    2 * Hkv * 128 * 2 bytes each (parallel samples that share a prompt block
+    count it once); plus q and out, one 4-byte block-table entry per logical
+    block and one context length per sequence; plus the copy-on-write pages
+    (read + write) and the new tokens' rows (read + write) and slots."""
     import numpy as np
 
     eb = 2
@@ -64,6 +68,34 @@ def step_bytes(wl, step):
     write = T * hkv * D * eb * 2 * 2 + T * 4  # K and V rows read + written, slots read
     return dict(kv_per_sequence=kv_seq, kv_unique=kv_unique, decode=decode, copy=copy, write=write,
                 step=decode + copy + write, q_out=qo, meta=meta)
+
+
+DECODE_SOURCES = ("paged_kv_cache_345_amd/csrc/decode.hip", "paged_kv_cache_345_amd/csrc/pkv_device.h",
+                  "paged_kv_cache_345_amd/csrc/pkv_launch.h", "paged_kv_cache_345_amd/csrc/api.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per paged_attn_decode call from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None
+    when there is no summary for this workload or the decode sources changed
+    since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path, encoding="utf-8"):
+        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_call", "sources_sha256"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("sources_sha256") != h.hexdigest() or "traffic_bytes_per_call" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_call"])
 
 
 def cpu_baseline(wl, seconds: float):
@@ -233,7 +265,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.spec.name),
         },
         "cpu_baseline": None,
     }
