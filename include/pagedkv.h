@@ -100,13 +100,18 @@ int64_t pkv_v_index(const pkv_cache_desc* cache, int32_t block, int32_t head, in
  *                 clamped to the table).
  *   scale         multiplies the logits before the softmax.
  *   num_kv_heads  must equal cache->num_kv_heads and divide num_heads.
- *   partition_tokens  0 = automatic; otherwise a multiple of 16 in [16, 1024]:
- *                 each sequence's context is split into partitions of this many
- *                 tokens whose softmax statistics are merged by a log-sum-exp
- *                 reduce kernel.
+ *   partition_tokens  0 = automatic; otherwise a multiple of 16 in [16, 4096]:
+ *                 each sequence's context is cut into segments of this many
+ *                 tokens; one work-group processes a segment, and a sequence
+ *                 with several segments has their softmax statistics merged by
+ *                 a log-sum-exp reduce kernel.  The automatic length depends
+ *                 on the shapes only (never on the GPU or the lengths).
  *   workspace     device scratch of at least paged_attn_decode_workspace_size()
- *                 bytes (may be NULL when that size is 0).  Owned by the caller;
- *                 contents on entry are irrelevant.
+ *                 bytes, 16-byte aligned (NULL only when that size is 0).
+ *                 Owned by the caller; contents on entry are irrelevant: the
+ *                 call first writes the work list of this batch there (a
+ *                 one-work-group pre-pass over context_lens), then the segment
+ *                 partials.
  * Calls on one stream are ordered; two calls sharing a workspace on different
  * streams race.  num_seqs == 0 is a no-op.
  * ------------------------------------------------------------------------- */
@@ -117,13 +122,34 @@ pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, cons
                              const pkv_cache_desc* cache, int32_t partition_tokens,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes paged_attn_decode needs for these arguments (0 when every
- * sequence fits one partition).  (size_t)-1 for invalid arguments. */
+/* paged_attn_decode split in two, for callers that decode several layers of
+ * one batch: the work list depends only on context_lens and the shapes, so
+ * paged_attn_decode_plan writes it into the workspace once, and
+ * paged_attn_decode_run then runs the attention of any number of layers (each
+ * with its own out, q and caches) from it.  Every run must use the same
+ * workspace, num_seqs, num_heads, max_blocks_per_seq, cache shape,
+ * partition_tokens and context_lens contents as the plan, and must follow it
+ * on the same stream (or be ordered after it); runs sharing one workspace
+ * must not overlap.  Arguments and errors as for paged_attn_decode. */
+pkv_status paged_attn_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                  int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                  int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+pkv_status paged_attn_decode_run(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 float scale, int32_t num_kv_heads,
+                                 int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                 const pkv_cache_desc* cache, int32_t partition_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes paged_attn_decode needs for these arguments: the work list
+ * (up to 4096 sequences) and, when a sequence can span several segments, the
+ * fp32 segment partials.  (size_t)-1 for invalid arguments. */
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
                                         int32_t max_blocks_per_seq, int32_t partition_tokens,
                                         const pkv_cache_desc* cache);
 
-/* Partition length in tokens that paged_attn_decode uses for these arguments
+/* Segment length in tokens that paged_attn_decode uses for these arguments
  * (resolves partition_tokens == 0).  -1 for invalid arguments. */
 int32_t paged_attn_decode_partition_tokens(int32_t num_seqs, int32_t num_heads,
                                            int32_t max_blocks_per_seq, int32_t partition_tokens,

@@ -62,6 +62,9 @@ SIGNATURES = {
     "pkv_v_index": (_i64, [_DP, _i32, _i32, _i32, _i32]),
     "paged_attn_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _i32,
                                  _vp, _sz, _vp]),
+    "paged_attn_decode_plan": (_i32, [_vp, _i32, _i32, _i32, _DP, _i32, _vp, _sz, _vp]),
+    "paged_attn_decode_run": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _i32,
+                                     _vp, _sz, _vp]),
     "paged_attn_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _DP]),
     "paged_attn_decode_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _DP]),
     "reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _DP, _vp]),
@@ -99,12 +102,18 @@ class OutOfBlocks(PagedKVError):
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded library; raises if it has not been built."""
+    """The loaded library; raises if it has not been built.
+
+    PyTorch is imported first: its wheel ships its own HIP and HSA runtimes,
+    and the library must bind to those (same soname) rather than load the
+    system copies beside them, which would leave two runtimes in one process
+    and device pointers from one used with the other."""
     global _LIB
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m paged_kv_cache_345_amd.build`")
+        _torch()
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)
@@ -218,9 +227,7 @@ def partition_tokens_for(num_seqs: int, num_heads: int, max_blocks_per_seq: int,
     return int(n)
 
 
-def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
-                      num_kv_heads: int, *, partition_tokens: int = 0, workspace=None, stream=None):
-    """out[s, h] = softmax(scale * q[s, h] . K[s, :ctx, h // g]) V[s, :ctx, h // g]."""
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, partition_tokens, workspace):
     torch = _torch()
     desc = _desc_of(k_cache)
     if desc.num_kv_heads != num_kv_heads:
@@ -243,10 +250,43 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_ptr = _gpu(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib().paged_attn_decode(*ptrs, float(scale), int(num_kv_heads), int(num_seqs), int(num_heads), mbps,
+    return ptrs, desc, num_seqs, num_heads, mbps, ws_ptr, ws_bytes
+
+
+def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                      num_kv_heads: int, *, partition_tokens: int = 0, workspace=None, stream=None):
+    """out[s, h] = softmax(scale * q[s, h] . K[s, :ctx, h // g]) V[s, :ctx, h // g]."""
+    ptrs, desc, S, Hq, mbps, ws_ptr, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                                             num_kv_heads, partition_tokens, workspace)
+    st = lib().paged_attn_decode(*ptrs, float(scale), int(num_kv_heads), int(S), int(Hq), mbps,
                                  ctypes.byref(desc), int(partition_tokens), ws_ptr, ws_bytes,
                                  _stream_handle(stream))
     _check(st, "paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_plan(context_lens, num_heads: int, max_blocks_per_seq: int, k_cache, workspace, *,
+                           partition_tokens: int = 0, stream=None):
+    """Write the work list of a batch into `workspace` (see paged_attn_decode_run)."""
+    torch = _torch()
+    desc = _desc_of(k_cache)
+    n = int(context_lens.shape[0])
+    st = lib().paged_attn_decode_plan(_gpu(context_lens, "context_lens", torch.int32, 1), n, int(num_heads),
+                                      int(max_blocks_per_seq), ctypes.byref(desc), int(partition_tokens),
+                                      _gpu(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                      _stream_handle(stream))
+    _check(st, "paged_attn_decode_plan")
+
+
+def paged_attn_decode_run(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                          num_kv_heads: int, *, workspace, partition_tokens: int = 0, stream=None):
+    """paged_attn_decode from a work list already written by paged_attn_decode_plan."""
+    ptrs, desc, S, Hq, mbps, ws_ptr, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                                             num_kv_heads, partition_tokens, workspace)
+    st = lib().paged_attn_decode_run(*ptrs, float(scale), int(num_kv_heads), int(S), int(Hq), mbps,
+                                     ctypes.byref(desc), int(partition_tokens), ws_ptr, ws_bytes,
+                                     _stream_handle(stream))
+    _check(st, "paged_attn_decode_run")
     return out
 
 
@@ -392,6 +432,7 @@ class BlockManager:
 __all__ = [
     "LIB_PATH", "BLOCK_SIZE", "HEAD_SIZE", "PAGE_ELEMS", "CacheDesc", "PagedKVError", "OutOfBlocks",
     "lib", "status_string", "version", "cache_desc", "allocate_cache", "k_index", "v_index",
-    "workspace_size", "partition_tokens_for", "paged_attn_decode", "reshape_and_cache", "copy_blocks",
+    "workspace_size", "partition_tokens_for", "paged_attn_decode", "paged_attn_decode_plan",
+    "paged_attn_decode_run", "reshape_and_cache", "copy_blocks",
     "gather_cache", "BlockManager", "SIGNATURES",
 ]

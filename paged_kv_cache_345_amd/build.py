@@ -23,11 +23,15 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "decode.hip", "cache_ops.hip", "block_manager.cpp"]
+SOURCES = ["api.hip", "decode.hip", "plan.hip", "cache_ops.hip", "block_manager.cpp"]
 
 COMMON = ["-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-fgpu-flush-denormals-to-zero", "-munsafe-fp-atomics"]
+# The decode kernels take work items with one atomic per item whose result is
+# consumed only after the item's page loads are issued; the compiler's
+# wave-level atomic rewriting would wait for it at once.
+PER_SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def hipcc() -> str:
@@ -41,7 +45,7 @@ def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
-        cmd = [hipcc(), "-x", "hip", *HIP_FLAGS, *COMMON, "-c", path, "-o", obj]
+        cmd = [hipcc(), "-x", "hip", *HIP_FLAGS, *PER_SOURCE_FLAGS.get(src, []), *COMMON, "-c", path, "-o", obj]
     else:
         cmd = ["g++", *COMMON, "-c", path, "-o", obj]
     if verbose:

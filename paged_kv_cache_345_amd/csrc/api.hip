@@ -28,18 +28,32 @@ pkv_status check_desc(const pkv_cache_desc* c) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Partition length in blocks.  Automatic choice: 16 blocks (256 tokens); 32
-// blocks (512 tokens) once a row can hold more than 8192 tokens; doubled
-// further only if the partition count would exceed the reduce kernel's bound.
-pkv_status resolve_partition(int32_t max_blocks_per_seq, int32_t partition_tokens, int32_t* bpp_out,
-                             int32_t* parts_out) {
+// MI355X: 256 compute units; work-groups of the decode kernels that fit on one
+// compute unit at once (4 waves each: MHA fp16 runs 5 waves per SIMD, MHA bf16
+// 4, the GQA kernel 2).
+constexpr int64_t kComputeUnits = 256;
+int64_t resident_work_groups(int32_t group, int32_t dtype) {
+  return kComputeUnits * (group == 1 ? (dtype == PKV_F16 ? 5 : 4) : 2);
+}
+
+// Segment length in blocks.  Automatic choice: the largest power of two in
+// [16, 128] blocks that is at most the expected work per resident work-group
+// (rows x max_blocks / 2 over the resident work-groups), so the longest items,
+// which run first, never outlast the rest; at least 16 blocks (4 per wave);
+// doubled (up to 256) only if the segment count would exceed the reduce
+// kernel's bound.  The choice depends on the shapes only, never on the GPU.
+pkv_status resolve_partition(int32_t num_seqs, int32_t units, int32_t group, int32_t dtype, int32_t max_blocks_per_seq,
+                             int32_t partition_tokens, int32_t* bpp_out, int32_t* parts_out) {
   int32_t bpp;
   if (partition_tokens == 0) {
-    bpp = max_blocks_per_seq > 512 ? 32 : 16;
-    while ((max_blocks_per_seq + bpp - 1) / bpp > pkv::kMaxPartitions && bpp < pkv::kMaxBlocksPerPartition) bpp *= 2;
+    const int64_t rows = static_cast<int64_t>(num_seqs) * units;
+    const int64_t per_wg = rows * max_blocks_per_seq / (2 * resident_work_groups(group, dtype));
+    bpp = 16;
+    while (bpp < 128 && 2 * bpp <= per_wg) bpp *= 2;
+    while ((max_blocks_per_seq + bpp - 1) / bpp > pkv::kMaxPartitions && bpp < pkv::kMaxSegmentBlocks) bpp *= 2;
   } else {
     if (partition_tokens < pkv::kBlockSize || partition_tokens % pkv::kBlockSize != 0 ||
-        partition_tokens > pkv::kBlockSize * pkv::kMaxBlocksPerPartition)
+        partition_tokens > pkv::kBlockSize * pkv::kMaxSegmentBlocks)
       return PKV_ERR_INVALID;
     bpp = partition_tokens / pkv::kBlockSize;
   }
@@ -60,10 +74,44 @@ pkv_status check_decode_shape(int32_t num_seqs, int32_t num_heads, int32_t max_b
   return PKV_OK;
 }
 
-size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t parts) {
-  if (parts <= 1) return 0;
-  const size_t rows = static_cast<size_t>(num_seqs) * static_cast<size_t>(num_heads) * static_cast<size_t>(parts);
-  return rows * (pkv::kHeadSize + 2) * sizeof(float);
+size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Workspace sections of one decode call, in bytes from its base.
+struct DecodeLayout {
+  int32_t bpp = 0, parts = 0, units = 0, group = 0;
+  bool planned = false;
+  size_t plan = 0, partial_o = 0, partial_ml = 0, total = 0;
+};
+
+pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq, int32_t partition_tokens,
+                         const pkv_cache_desc* cache, DecodeLayout* out) {
+  pkv_status st = check_decode_shape(num_seqs, num_heads, max_blocks_per_seq, cache);
+  if (st != PKV_OK) return st;
+  DecodeLayout L;
+  L.group = num_heads / cache->num_kv_heads;
+  L.units = cache->num_kv_heads * (L.group == 1 ? 1 : (L.group + 15) / 16);
+  st = resolve_partition(num_seqs, L.units, L.group, cache->dtype, max_blocks_per_seq, partition_tokens, &L.bpp,
+                         &L.parts);
+  if (st != PKV_OK) return st;
+  const int64_t chunks = (static_cast<int64_t>(num_seqs) + 63) / 64;
+  L.planned = num_seqs <= pkv::kPlanMaxSeqs && (static_cast<int64_t>(L.parts) + L.bpp) * chunks <= pkv::kPlanMaxTasks &&
+              static_cast<int64_t>(L.units) * num_seqs * L.parts < (int64_t{1} << 31);
+  const size_t S = static_cast<size_t>(num_seqs);
+  size_t off = 0;
+  if (L.planned) {
+    L.plan = off;
+    off += round_up((pkv::kPlanHeaderInts + S * static_cast<size_t>(L.parts) + S) * sizeof(int32_t));
+  }
+  if (L.parts > 1) {
+    const size_t rows = S * static_cast<size_t>(num_heads) * static_cast<size_t>(L.parts);
+    L.partial_o = off;
+    off += round_up(rows * pkv::kHeadSize * sizeof(float));
+    L.partial_ml = off;
+    off += round_up(rows * 2 * sizeof(float));
+  }
+  L.total = off;
+  *out = L;
+  return PKV_OK;
 }
 
 pkv_status from_hip(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_DEVICE; }
@@ -93,38 +141,62 @@ int64_t pkv_v_index(const pkv_cache_desc* c, int32_t block, int32_t head, int32_
 
 int32_t paged_attn_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                            int32_t partition_tokens, const pkv_cache_desc* cache) {
-  if (check_decode_shape(num_seqs, num_heads, max_blocks_per_seq, cache) != PKV_OK) return -1;
-  int32_t bpp, parts;
-  if (resolve_partition(max_blocks_per_seq, partition_tokens, &bpp, &parts) != PKV_OK) return -1;
-  return bpp * pkv::kBlockSize;
+  DecodeLayout L;
+  if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, partition_tokens, cache, &L) != PKV_OK) return -1;
+  return L.bpp * pkv::kBlockSize;
 }
 
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                         int32_t partition_tokens, const pkv_cache_desc* cache) {
-  if (check_decode_shape(num_seqs, num_heads, max_blocks_per_seq, cache) != PKV_OK) return static_cast<size_t>(-1);
-  int32_t bpp, parts;
-  if (resolve_partition(max_blocks_per_seq, partition_tokens, &bpp, &parts) != PKV_OK) return static_cast<size_t>(-1);
-  return workspace_bytes_for(num_seqs, num_heads, parts);
+  DecodeLayout L;
+  if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, partition_tokens, cache, &L) != PKV_OK)
+    return static_cast<size_t>(-1);
+  return L.total;
 }
 
-pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                             const int32_t* block_tables, const int32_t* context_lens, float scale,
-                             int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
-                             const pkv_cache_desc* cache, int32_t partition_tokens, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the plan and the run entry points.
+pkv_status check_workspace(const DecodeLayout& L, const void* workspace, size_t workspace_bytes) {
+  if (L.total > 0 && (!workspace || workspace_bytes < L.total || !aligned16(workspace))) return PKV_ERR_INVALID;
+  return PKV_OK;
+}
+
+pkv_status launch_plan(const DecodeLayout& L, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t max_blocks_per_seq, void* workspace, hipStream_t stream) {
+  if (!L.planned) return PKV_OK;
+  pkv::PlanArgs pa;
+  pa.context_lens = context_lens;
+  pa.plan = reinterpret_cast<int*>(static_cast<char*>(workspace) + L.plan);
+  pa.num_seqs = num_seqs;
+  pa.num_heads = num_heads;
+  pa.units = L.units;
+  pa.max_blocks_per_seq = max_blocks_per_seq;
+  pa.blocks_per_part = L.bpp;
+  pa.parts_max = L.parts;
+  return from_hip(pkv::launch_decode_plan(pa, stream));
+}
+
+pkv_status decode_impl(bool plan_first, void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t num_kv_heads,
+                       int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                       int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
   pkv_status st = check_decode_shape(num_seqs, num_heads, max_blocks_per_seq, cache);
   if (st != PKV_OK) return st;
   if (num_kv_heads != cache->num_kv_heads) return PKV_ERR_INVALID;
   if (!std::isfinite(scale)) return PKV_ERR_INVALID;
-  int32_t bpp, parts;
-  st = resolve_partition(max_blocks_per_seq, partition_tokens, &bpp, &parts);
+  DecodeLayout L;
+  st = decode_layout(num_seqs, num_heads, max_blocks_per_seq, partition_tokens, cache, &L);
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID;
-  const size_t need = workspace_bytes_for(num_seqs, num_heads, parts);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PKV_ERR_INVALID;
+  st = check_workspace(L, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
 
+  char* ws = static_cast<char*>(workspace);
   pkv::DecodeArgs a;
   a.out = static_cast<uint16_t*>(out);
   a.q = static_cast<const uint16_t*>(q);
@@ -132,20 +204,63 @@ pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, cons
   a.v_cache = static_cast<const uint16_t*>(v_cache);
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  const size_t rows = static_cast<size_t>(num_seqs) * static_cast<size_t>(num_heads) * static_cast<size_t>(parts);
-  a.ws_o = need ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = need ? static_cast<float*>(workspace) + rows * pkv::kHeadSize : nullptr;
+  a.ws_o = L.parts > 1 ? reinterpret_cast<float*>(ws + L.partial_o) : nullptr;
+  a.ws_ml = L.parts > 1 ? reinterpret_cast<float*>(ws + L.partial_ml) : nullptr;
+  a.plan = L.planned ? reinterpret_cast<int*>(ws + L.plan) : nullptr;
   a.scale_log2e = static_cast<float>(static_cast<double>(scale) * kLog2e);
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
-  a.group = num_heads / num_kv_heads;
-  a.head_tiles = (a.group + 15) / 16;
+  a.group = L.group;
+  a.head_tiles = (L.group + 15) / 16;
+  a.units = L.units;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = cache->num_blocks;
-  a.blocks_per_part = bpp;
-  a.parts_max = parts;
-  return from_hip(pkv::launch_decode(a, cache->dtype, static_cast<hipStream_t>(stream)));
+  a.blocks_per_part = L.bpp;
+  a.parts_max = L.parts;
+  a.planned = L.planned ? 1 : 0;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (plan_first) {
+    st = launch_plan(L, context_lens, num_seqs, num_heads, max_blocks_per_seq, workspace, hs);
+    if (st != PKV_OK) return st;
+  }
+  return from_hip(pkv::launch_decode(a, cache->dtype, hs));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens, float scale,
+                             int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                             const pkv_cache_desc* cache, int32_t partition_tokens, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return decode_impl(true, out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, num_seqs,
+                     num_heads, max_blocks_per_seq, cache, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pkv_status paged_attn_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                  int32_t max_blocks_per_seq, const pkv_cache_desc* cache, int32_t partition_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeLayout L;
+  pkv_status st = decode_layout(num_seqs, num_heads, max_blocks_per_seq, partition_tokens, cache, &L);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!context_lens) return PKV_ERR_INVALID;
+  st = check_workspace(L, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  return launch_plan(L, context_lens, num_seqs, num_heads, max_blocks_per_seq, workspace,
+                     static_cast<hipStream_t>(stream));
+}
+
+pkv_status paged_attn_decode_run(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                 int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                                 int32_t max_blocks_per_seq, const pkv_cache_desc* cache, int32_t partition_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(false, out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, num_seqs,
+                     num_heads, max_blocks_per_seq, cache, partition_tokens, workspace, workspace_bytes, stream);
 }
 
 pkv_status reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,

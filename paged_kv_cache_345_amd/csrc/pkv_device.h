@@ -27,8 +27,9 @@ constexpr int kPageElems = kBlockSize * kHeadSize;  // 2048
 constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 4;                   // decode work-groups: 4 independent waves
 constexpr int kNumXcd = 8;                          // MI355X: 8 XCDs, work-groups dealt round-robin
-constexpr int kMaxPartitions = 4096;                // reduce kernel LDS bound
-constexpr int kMaxBlocksPerPartition = 64;          // one block id per lane
+constexpr int kMaxPartitions = 4096;                // segments per row (reduce kernel LDS bound)
+constexpr int kMaxBlocksPerWave = 64;              // one block id per lane
+constexpr int kMaxSegmentBlocks = kWavesPerGroup * kMaxBlocksPerWave;  // 256
 constexpr float kMaskedLogit = -__builtin_inff();
 constexpr float kInitMax = -1.0e30f;                // finite: exp2(kInitMax - kInitMax) == 1
 
@@ -51,6 +52,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // Element-type traits.  Storage is 16-bit words; arithmetic is fp32.
 // ---------------------------------------------------------------------------
 struct F16 {
+  static constexpr int kMhaWavesPerSimd = 5;  // MHA decode fits 5 waves per SIMD (<= 102 VGPRs)
   __device__ static inline float lo(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[0]; }
   __device__ static inline float hi(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[1]; }
   __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
@@ -73,6 +75,7 @@ struct F16 {
 };
 
 struct BF16 {
+  static constexpr int kMhaWavesPerSimd = 4;  // the bf16 widening needs more registers
   __device__ static inline float lo(uint32_t w) { return __uint_as_float(w << 16); }
   __device__ static inline float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
   __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {

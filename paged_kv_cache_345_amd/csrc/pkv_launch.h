@@ -1,5 +1,5 @@
 // Host-side launch interface between the C ABI (api.hip) and the kernel
-// translation units (decode.hip, cache_ops.hip).
+// translation units (decode.hip, plan.hip, cache_ops.hip).
 
 #pragma once
 
@@ -8,6 +8,22 @@
 
 namespace pkv {
 
+// Work-list plan of one decode call, written by decode_plan_kernel into the
+// caller's workspace and read by the decode kernels.  A work item is one
+// segment (blocks_per_part consecutive blocks) of one row (sequence, unit).
+// Int offsets into `plan`:
+constexpr int kPlanFull = 0;         // F: full segments per unit
+constexpr int kPlanPartial = 1;      // P: partial (last) segments per unit
+constexpr int kPlanClasses = 256;    // partial-size classes (segments hold at most 256 blocks)
+constexpr int kPlanClassOff = 16;    // [16, 16 + kPlanClasses]: class offsets into list B
+constexpr int kPlanHeaderInts = 512;
+// list_A (F entries, packed s | g << 20) follows the header; list_B (one
+// sequence id per partial segment, P entries) follows list_A's capacity of
+// num_seqs * parts_max entries.
+constexpr int kPlanSeqBits = 20;
+constexpr int kPlanMaxSeqs = 4096;   // sequences one plan covers (LDS bound)
+constexpr int kPlanMaxTasks = 6144;  // (segments + size classes) x 64-sequence chunks (LDS bound)
+
 struct DecodeArgs {
   uint16_t* out;
   const uint16_t* q;
@@ -15,21 +31,36 @@ struct DecodeArgs {
   const uint16_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_o;   // [S, Hq, parts_max, 128] unnormalised partial outputs
-  float* ws_ml;  // [S, Hq, parts_max, 2]   (running max in log2 units, Z)
+  float* ws_o;     // [S, Hq, parts_max, 128] unnormalised partial outputs
+  float* ws_ml;    // [S, Hq, parts_max, 2]   (running max in log2 units, Z)
+  int* plan;       // work-list plan (planned mode) or null
   float scale_log2e;
   int num_seqs;
   int num_heads;
   int num_kv_heads;
   int group;       // num_heads / num_kv_heads
   int head_tiles;  // ceil(group / 16)
+  int units;       // work units per sequence: num_kv_heads * (group == 1 ? 1 : head_tiles)
   int max_blocks_per_seq;
   int num_blocks;
+  int blocks_per_part;  // segment length in blocks (<= 4 x 64: each wave streams at most 64)
+  int parts_max;        // segments of the longest possible row
+  int planned;  // 1: items come from the plan's work list; 0: from blockIdx directly
+};
+
+struct PlanArgs {
+  const int32_t* context_lens;
+  int* plan;
+  int num_seqs;
+  int num_heads;
+  int units;
+  int max_blocks_per_seq;
   int blocks_per_part;
   int parts_max;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_decode_plan(const PlanArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                                     int32_t num_blocks, hipStream_t stream);

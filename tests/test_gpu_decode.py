@@ -202,3 +202,94 @@ def test_full_size_sampled(name):
         ref = _ref_seq(wl, s, heads)
         err = np.abs(got[s, heads] - ref).max()
         assert err <= TOL[wl.dtype], (s, err)
+
+
+def _plan_ref(lens, bpp, max_blocks):
+    """The work list the plan must hold, from its definition: list A has every
+    full segment (p, s), p < nblk_s // bpp, in (p, s) order; list B has the
+    sequences whose last segment is partial, by partial size descending, then
+    by sequence, and then the sequences with an empty context."""
+    nblk = [min(-(-int(L) // 16), max_blocks) for L in lens]
+    list_a = [(s, p) for p in range(max(n // bpp for n in nblk) if nblk else 0)
+              for s in range(len(nblk)) if nblk[s] // bpp > p]
+    list_b = [s for r in range(bpp - 1, 0, -1) for s in range(len(nblk)) if nblk[s] % bpp == r]
+    list_b += [s for s in range(len(nblk)) if nblk[s] == 0]  # empty contexts come last
+    return list_a, list_b
+
+
+@pytest.mark.parametrize("name,pt", [("llama13b", 0), ("random", 48), ("random", 16)])
+def test_plan_lists_are_exact(name, pt):
+    """White-box check of the work-list pre-pass (integer work, bit-exact): the
+    plan at the start of the workspace lists every non-empty partition once, in
+    the documented order."""
+    if name == "llama13b":
+        wl = synth.make_workload("llama13b")
+    else:
+        wl = synth.make_random_workload(4242 + pt, num_seqs=70, num_heads=4, num_kv_heads=2, dtype="fp16",
+                                        max_len=900, min_len=1, groups=3)
+    step = harness.build_step(wl, partition_tokens=pt)
+    desc = step.desc
+    S = wl.num_seqs
+    bpp = pkv.partition_tokens_for(S, wl.num_heads, step.max_blocks, desc, pt) // 16
+    parts = -(-step.max_blocks // bpp)
+    ws = torch.empty(pkv.workspace_size(S, wl.num_heads, step.max_blocks, desc, pt), dtype=torch.uint8,
+                     device="cuda")
+    ws.fill_(0xAB)
+    lens = wl.context_lens.copy()
+    ctx = step.context_lens.clone()
+    if name == "random":  # two empty contexts exercise the last class of list B
+        lens[[3, 40]] = 0
+        ctx[[3, 40]] = 0
+    out = torch.full_like(step.out, 7.0)
+    pkv.paged_attn_decode(out, step.q, step.k_cache, step.v_cache, step.block_tables, ctx, wl.scale,
+                          wl.num_kv_heads, partition_tokens=pt, workspace=ws)
+    torch.cuda.synchronize()
+    H0 = 512  # header ints
+    plan = ws[: (H0 + S * parts + S) * 4].view(torch.int32).cpu().numpy()
+    ref_a, ref_b = _plan_ref(lens, bpp, step.max_blocks)
+    F, NB = int(plan[0]), int(plan[1])
+    assert F == len(ref_a) and NB == len(ref_b)
+    got_a = [(int(v) & 0xFFFFF, int(v) >> 20) for v in plan[H0:H0 + F]]
+    assert got_a == ref_a
+    got_b = [int(v) for v in plan[H0 + S * parts:H0 + S * parts + NB]]
+    assert got_b == ref_b
+    if name == "random":
+        assert (out[[3, 40]] == 0).all()
+
+
+@pytest.mark.parametrize("g,pt", [(1, 0), (1, 64), (4, 0), (8, 512)])
+def test_plan_once_run_many_layers(g, pt):
+    """One plan serves several layers: run() with two different queries and
+    caches is bit-identical to paged_attn_decode on each."""
+    dtype = "bf16" if g > 1 else "fp16"
+    wl = synth.make_random_workload(6100 + g + pt, num_seqs=9, num_heads=2 * g, num_kv_heads=2, dtype=dtype,
+                                    max_len=1500, min_len=1, groups=1)
+    a = harness.build_step(wl, partition_tokens=pt)
+    b = harness.build_step(dataclasses.replace(wl, q=wl.q[::-1].copy()), partition_tokens=pt)
+    ws = torch.empty(pkv.workspace_size(wl.num_seqs, wl.num_heads, a.max_blocks, a.desc, pt), dtype=torch.uint8,
+                     device="cuda")
+    pkv.paged_attn_decode_plan(a.context_lens, wl.num_heads, a.max_blocks, a.k_cache, ws, partition_tokens=pt)
+    outs = []
+    for st in (a, b):
+        o = torch.empty_like(st.out)
+        pkv.paged_attn_decode_run(o, st.q, st.k_cache, st.v_cache, st.block_tables, st.context_lens, wl.scale,
+                                  wl.num_kv_heads, workspace=ws, partition_tokens=pt)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for st, o in zip((a, b), outs):
+        assert torch.equal(o.view(torch.int16), st.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("num_seqs", [4096, 4100])
+@pytest.mark.parametrize("g", [1, 4])
+def test_many_sequences_planned_and_direct(num_seqs, g):
+    """4096 sequences is the largest batch the work-list plan covers; one more
+    takes the direct path.  Both must match the oracle on every sequence."""
+    wl = synth.make_random_workload(5100 + num_seqs + g, num_seqs=num_seqs, num_heads=2 * g, num_kv_heads=2,
+                                    dtype="fp16", max_len=40, min_len=1)
+    step = harness.build_step(wl)
+    got = _out_f64(step.out, "fp16")
+    worst = 0.0
+    for s in range(num_seqs):
+        worst = max(worst, float(np.abs(got[s] - _ref_seq(wl, s)).max()))
+    assert worst <= TOL["fp16"], worst
