@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the paged KV cache hot path on one MI355X.
 
-One step = the three GPU calls of a decode step over one synthetic batch with
-every input already resident in HBM: copy_blocks (copy-on-write pairs),
-reshape_and_cache (the new tokens) and paged_attn_decode (split into
-partitions and merged by the log-sum-exp reduce when a row spans several).
+One step = the GPU calls of a decode step over one synthetic batch with every
+input already resident in HBM: copy_blocks (copy-on-write pairs),
+reshape_and_cache (the new tokens), paged_attn_decode_plan (the batch's work
+list) and paged_attn_decode_run (the attention; segments of long rows merged
+by the log-sum-exp reduce).  The roofline figure is for the attention run
+alone, timed with HIP events on the stream it runs on.
 Default workload: the LLaMA-13B-shaped batch (128 sequences, 40 MHA heads,
 head 128, block 16, fp16, lognormal contexts with median 600 capped at 2048,
 13 groups of 3 parallel samples sharing prompt blocks).
@@ -196,7 +198,10 @@ def main() -> int:
     nb = step_bytes(wl, step)
 
     for _ in range(args.warmup):
-        step.run_step()
+        step.copy()
+        step.write()
+        step.plan()
+        step.run()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -210,8 +215,9 @@ def main() -> int:
     for i in range(K):
         step.copy()
         step.write()
+        step.plan()
         dec_start[i].record()
-        step.decode()
+        step.run()
         dec_end[i].record()
     all_end.record()
     torch.cuda.synchronize()
@@ -222,6 +228,8 @@ def main() -> int:
     log(f"step {ms_per_step * 1e3:.1f} us (wall {wall_s / K * 1e6:.1f} us); decode avg {dec_avg * 1e3:.1f} us, "
         f"min {min(dec_ms) * 1e3:.1f} us")
 
+    seg_tokens = pkv.partition_tokens_for(wl.num_seqs, wl.num_heads, step.max_blocks, step.desc,
+                                          step.partition_tokens)
     step_gbs = nb["step"] / (ms_per_step * 1e-3) / 1e9
     dec_gbs = nb["decode"] / (dec_avg * 1e-3) / 1e9
     S = wl.num_seqs
@@ -250,7 +258,7 @@ def main() -> int:
             "partition_tokens": pkv.partition_tokens_for(S, wl.num_heads, step.max_blocks, step.desc,
                                                          step.partition_tokens),
             "copy_pairs": int(step.block_pairs_host.shape[0]),
-            "step": "copy_blocks + reshape_and_cache + paged_attn_decode",
+            "step": "copy_blocks + reshape_and_cache + paged_attn_decode_plan + paged_attn_decode_run",
             "parallelism": "single GPU",
         },
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
@@ -260,7 +268,9 @@ def main() -> int:
         "decode_call_us": round(dec_avg * 1e3, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attn_decode (decode kernel + log-sum-exp reduce)",
+            "kernel": ("paged_attn_decode_run: " + ("decode_mha_kernel" if wl.num_heads == wl.num_kv_heads
+                                                    else "decode_gqa_kernel")
+                       + (" + decode_reduce_kernel" if step.max_blocks * 16 > seg_tokens else "")),
             "achieved": round(dec_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -87,6 +87,19 @@ class GpuStep:
                               partition_tokens=pt, workspace=ws, stream=stream)
         return out
 
+    def plan(self, stream=None):
+        """Work list of the batch into the step's workspace (paged_attn_decode_plan)."""
+        pkv.paged_attn_decode_plan(self.context_lens, self.wl.num_heads, self.max_blocks, self.k_cache,
+                                   self.workspace, partition_tokens=self.partition_tokens, stream=stream)
+
+    def run(self, out=None, stream=None):
+        """Attention from the planned work list (paged_attn_decode_run)."""
+        out = self.out if out is None else out
+        pkv.paged_attn_decode_run(out, self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
+                                  self.wl.scale, self.wl.num_kv_heads, workspace=self.workspace,
+                                  partition_tokens=self.partition_tokens, stream=stream)
+        return out
+
     def run_step(self, stream=None):
         self.copy(stream)
         self.write(stream)

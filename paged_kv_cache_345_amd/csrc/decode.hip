@@ -156,18 +156,18 @@ __device__ inline void load_page(uint4 (&kv)[4], uint4 (&vv)[4], const uint16_t*
   vv[3] = load16<3072>(vr, lane_bytes);
 }
 
-// Streams blocks j0 .. j0 + nb - 1 (1 <= nb <= 64) of one sequence's pages of
-// one KV head through `process`, two register sets deep: one block in flight
-// while the other is consumed.  Only the last block takes the masked path.
+// Streams blocks j0 .. j0 + nb - 1 (nb >= 1) of one sequence's pages of one KV
+// head through `process`, two register sets deep: one block in flight while
+// the other is consumed.  Only the last block takes the masked path.  Block
+// ids are wave-uniform scalar loads (16 per scalar-cache line).
 template <class Process>
 __device__ __attribute__((always_inline)) inline void stream_blocks(const DecodeArgs& a, int s, int kvh, int j0, int nb,
                                                                     int lane, Process&& process) {
-  int my_bid = 0;
-  if (lane < nb) my_bid = a.block_tables[static_cast<int64_t>(s) * a.max_blocks_per_seq + j0 + lane];
+  const int32_t* row = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq + j0;
   const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kPageElems;
   const int64_t head_off = static_cast<int64_t>(kvh) * kPageElems;
   auto issue = [&](uint4 (&kv)[4], uint4 (&vv)[4], int jj) __attribute__((always_inline)) {
-    const int bid = __builtin_amdgcn_readlane(my_bid, jj);
+    const int bid = row[jj];
     const bool bad = static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks);
     const int64_t off = static_cast<int64_t>(bad ? 0 : bid) * page_stride + head_off;
     load_page(kv, vv, a.k_cache + off, a.v_cache + off, static_cast<uint32_t>(lane) * 16u);
@@ -219,14 +219,16 @@ __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(D
   if (!work_group_item(a, s, h, g)) return;  // uniform over the work-group
   const int lane = threadIdx.x & 63;
   const int wave = wave_id_uniform();
-  const int L = clamped_len(a, s);
-  const int nblk = (L + kBlockSize - 1) / kBlockSize;
+  const int nblk = (clamped_len(a, s) + kBlockSize - 1) / kBlockSize;
   const WaveRange wr = wave_range(a, nblk, g, wave);
-  uint16_t* out_row = a.out + (static_cast<int64_t>(s) * a.num_heads + h) * kHeadSize;
   if (g >= wr.nseg) {  // direct mode past the row's end (uniform over the work-group)
-    if (g == 0 && threadIdx.x < kHeadSize) out_row[threadIdx.x] = 0;  // empty context: zero row
+    if (g == 0 && threadIdx.x < kHeadSize)  // empty context: zero row
+      a.out[(static_cast<int64_t>(s) * a.num_heads + h) * kHeadSize + threadIdx.x] = 0;
     return;
   }
+  const int row_s = s, j_begin = wr.j0, j_count = wr.nb, nseg = wr.nseg;
+  const int L = clamped_len(a, row_s);
+  uint16_t* out_row = a.out + (static_cast<int64_t>(row_s) * a.num_heads + h) * kHeadSize;
   const int grp = lane >> 4;
   const int col = lane & 15;
 
@@ -236,9 +238,9 @@ __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(D
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 
-  if (wr.nb > 0) {
+  if (j_count > 0) {
     const uint4* qrow =
-        reinterpret_cast<const uint4*>(a.q + (static_cast<int64_t>(s) * a.num_heads + h) * kHeadSize);
+        reinterpret_cast<const uint4*>(a.q + (static_cast<int64_t>(row_s) * a.num_heads + h) * kHeadSize);
     uint4 qf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) qf[i] = qrow[4 * i + grp];
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(D
         }
       }
     };
-    stream_blocks(a, s, h, wr.j0, wr.nb, lane, process);
+    stream_blocks(a, row_s, h, j_begin, j_count, lane, process);
     z = row_sum16(z);
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = cross_row_sum(acc[j]);
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(D
       Z = fmaf(c, red_z[w], Z);
       O = fmaf(c, red_o[w][d], O);
     }
-    if (wr.nseg == 1) {
+    if (nseg == 1) {
       out_row[d] = DT::from_f32(O / Z);
     } else {
       const int64_t slot = (static_cast<int64_t>(s) * a.num_heads + h) * a.parts_max + g;

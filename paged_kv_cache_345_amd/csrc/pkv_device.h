@@ -28,8 +28,7 @@ constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 4;                   // decode work-groups: 4 independent waves
 constexpr int kNumXcd = 8;                          // MI355X: 8 XCDs, work-groups dealt round-robin
 constexpr int kMaxPartitions = 4096;                // segments per row (reduce kernel LDS bound)
-constexpr int kMaxBlocksPerWave = 64;              // one block id per lane
-constexpr int kMaxSegmentBlocks = kWavesPerGroup * kMaxBlocksPerWave;  // 256
+constexpr int kMaxSegmentBlocks = 256;             // segment length bound (4096 tokens)
 constexpr float kMaskedLogit = -__builtin_inff();
 constexpr float kInitMax = -1.0e30f;                // finite: exp2(kInitMax - kInitMax) == 1
 

@@ -14,12 +14,12 @@ namespace pkv {
 // Int offsets into `plan`:
 constexpr int kPlanFull = 0;         // F: full segments per unit
 constexpr int kPlanPartial = 1;      // P: partial (last) segments per unit
-constexpr int kPlanClasses = 256;    // partial-size classes (segments hold at most 256 blocks)
+constexpr int kPlanClasses = 32;     // list B classes: up to 16 partial-size buckets and the empties (power of 2)
 constexpr int kPlanClassOff = 16;    // [16, 16 + kPlanClasses]: class offsets into list B
 constexpr int kPlanHeaderInts = 512;
 // list_A (F entries, packed s | g << 20) follows the header; list_B (one
-// sequence id per partial segment, P entries) follows list_A's capacity of
-// num_seqs * parts_max entries.
+// sequence id per partial segment or empty sequence, P entries) follows
+// list_A's capacity of num_seqs * parts_max entries.
 constexpr int kPlanSeqBits = 20;
 constexpr int kPlanMaxSeqs = 4096;   // sequences one plan covers (LDS bound)
 constexpr int kPlanMaxTasks = 6144;  // (segments + size classes) x 64-sequence chunks (LDS bound)

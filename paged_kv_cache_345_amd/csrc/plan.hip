@@ -5,16 +5,17 @@
 // The plan orders the items so that
 //   * the large items come first and the small ones last: every full
 //     segment (list A) precedes the sequences' partial last segments
-//     (list B), and list B runs from the largest partial size to the smallest,
-//     so the kernel's tail consists of the shortest items;
+//     (list B), and list B runs from the largest partial sizes to the
+//     smallest, so the kernel's tail consists of the shortest items;
 //   * parallel samples, which are consecutive sequences with equal lengths and
 //     shared prompt blocks, sit next to each other in both lists and are read
 //     by neighbouring waves at about the same time;
 //   * no empty item exists, so no work-group is dispatched only to exit.
 //
 // List A, per unit, in the order (segment p, sequence s) over the pairs with
-// p < f_s = nblk_s / blocks_per_part.  List B, per size class r (partial size,
-// descending), the sequences with nblk_s % blocks_per_part == r in order.  The
+// p < f_s = nblk_s / blocks_per_part.  List B, per class of partial size r =
+// nblk_s % blocks_per_part (largest first), the sequences of that class in
+// order, then the sequences with an empty context.  The
 // positions come from per-(segment, 64-sequence chunk) counts and a prefix
 // over chunks; a wave ballot gives each sequence its rank inside a chunk.
 //
@@ -35,10 +36,16 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / kWave;
 constexpr int kRBits = 8;  // blocks_per_part <= 256, so a remainder fits 8 bits
 
-// List B classes, in order: partial segments of bpp - 1, bpp - 2, ..., 1
-// blocks, then the empty sequences (no blocks: their item writes the defined
-// zero output row).
-__device__ inline int class_of(int r, int bpp) { return r ? bpp - 1 - r : bpp - 1; }
+// List B classes, in order: partial segments by size, largest first, in
+// kSizeBuckets buckets (one size per bucket when blocks_per_part <= 16), then
+// the empty sequences (no blocks: their item writes the defined zero output
+// row).
+constexpr int kSizeBuckets = kPlanClasses / 2;
+__device__ inline int num_classes(int bpp) { return (bpp - 1 < kSizeBuckets ? bpp - 1 : kSizeBuckets) + 1; }
+__device__ inline int class_of(int r, int bpp) {
+  const int nb = num_classes(bpp) - 1;
+  return r ? ((bpp - 1 - r) * nb) / (bpp - 1) : nb;
+}
 __device__ inline bool in_class(int fr, int c, int bpp) {
   const int r = fr & ((1 << kRBits) - 1);
   const int f = fr >> kRBits;
@@ -69,10 +76,10 @@ __device__ int wave_exclusive_scan(int* x, int n, int lane) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(PlanArgs a) {
-  __shared__ int fr[kPlanMaxSeqs];                    // f << kRBits | r per sequence
-  __shared__ int hist_f[kMaxPartitions + 2];          // count of f, then prefix data
-  __shared__ int cnt[kPlanMaxTasks];                  // per (partition | class, chunk) counts
-  __shared__ int cls_off[kPlanClasses + 1];           // partial classes, size descending
+  __shared__ int fr[kPlanMaxSeqs];            // f << kRBits | r per sequence
+  __shared__ int hist_f[kMaxPartitions + 2];  // count of f, then prefix data
+  __shared__ int cnt[kPlanMaxTasks];          // per (segment | class, chunk) counts
+  __shared__ int cls_off[kPlanClasses + 1];   // partial classes, size descending
   __shared__ int f_max;
   __shared__ int full_total;
 
@@ -89,9 +96,10 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(PlanArgs a) {
   for (int i = tid; i <= a.parts_max + 1; i += kPlanThreads) hist_f[i] = 0;
   for (int i = tid; i <= kPlanClasses; i += kPlanThreads) cls_off[i] = 0;
   if (tid == 0) f_max = 0;
+
   __syncthreads();
 
-  // per-sequence block counts
+  // per-sequence segment counts
   for (int s = tid; s < S; s += kPlanThreads) {
     int L = a.context_lens[s];
     L = L < 0 ? 0 : L;
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(PlanArgs a) {
   __syncthreads();
 
   const int P = f_max;
-  const int nclass = bpp;
+  const int nclass = num_classes(bpp);
   // c_p = #{s : f_s > p} = S - #{s : f_s <= p}, and list A offsets C_p = prefix of c_p
   if (wave == 0) wave_exclusive_scan(hist_f, P + 1, lane);  // hist_f[x] = #{s : f_s < x}
   __syncthreads();

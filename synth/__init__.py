@@ -335,18 +335,21 @@ def make_workload(name_or_spec, *, with_q: bool = True) -> Workload:
 
 def make_random_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_heads: int,
                          dtype: str, max_len: int, pool_slack: int = 4,
-                         min_len: int = 1, groups: int = 0, key_scale=None) -> Workload:
+                         min_len: int = 1, groups: int = 0, group_size: int = 3,
+                         key_scale=None) -> Workload:
     """Small random workload for property tests: lengths U[min_len, max_len],
-    optionally the first 3*groups sequences in sampling groups of 3."""
+    optionally the first group_size*groups sequences in sampling groups of
+    group_size."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(min_len, max_len, num_seqs, endpoint=True).astype(np.int64)
     grp = []
+    n = group_size
     for g in range(groups):
-        plen = int(max(1, min(lens[3 * g], max_len) - 1))
-        grp.append((3 * g, 3, plen))
-        lens[3 * g:3 * g + 3] = plen + 1
+        plen = int(max(1, min(lens[n * g], max_len) - 1))
+        grp.append((n * g, n, plen))
+        lens[n * g:n * g + n] = plen + 1
     # generous pool: every token its own block would still fit
-    pool = int(sum(-(-int(v) // BLOCK_SIZE) + 1 for v in lens)) + 3 * groups + pool_slack
+    pool = int(sum(-(-int(v) // BLOCK_SIZE) + 1 for v in lens)) + n * groups + pool_slack
     spec = ConfigSpec(name=f"random{seed}", seed=seed, num_seqs=num_seqs, num_heads=num_heads,
                       num_kv_heads=num_kv_heads, dtype=dtype,
                       lengths=("fixed", tuple(int(v) for v in lens)), pool_blocks=pool,

@@ -207,26 +207,32 @@ def test_full_size_sampled(name):
 def _plan_ref(lens, bpp, max_blocks):
     """The work list the plan must hold, from its definition: list A has every
     full segment (p, s), p < nblk_s // bpp, in (p, s) order; list B has the
-    sequences whose last segment is partial, by partial size descending, then
-    by sequence, and then the sequences with an empty context."""
+    sequences whose last segment is partial, by class of partial size (16
+    classes at most, largest sizes first), then by sequence, and then the
+    sequences with an empty context."""
+    S = len(lens)
     nblk = [min(-(-int(L) // 16), max_blocks) for L in lens]
-    list_a = [(s, p) for p in range(max(n // bpp for n in nblk) if nblk else 0)
-              for s in range(len(nblk)) if nblk[s] // bpp > p]
-    list_b = [s for r in range(bpp - 1, 0, -1) for s in range(len(nblk)) if nblk[s] % bpp == r]
-    list_b += [s for s in range(len(nblk)) if nblk[s] == 0]  # empty contexts come last
+    P = max([n // bpp for n in nblk], default=0)
+    list_a = [(s, p) for p in range(P) for s in range(S) if nblk[s] // bpp > p]
+    nb = min(bpp - 1, 16)
+    def cls(r):
+        return ((bpp - 1 - r) * nb) // (bpp - 1)
+    list_b = [s for c in range(nb) for s in range(S) if nblk[s] % bpp and cls(nblk[s] % bpp) == c]
+    list_b += [s for s in range(S) if nblk[s] == 0]  # empty contexts come last
     return list_a, list_b
 
 
-@pytest.mark.parametrize("name,pt", [("llama13b", 0), ("random", 48), ("random", 16)])
-def test_plan_lists_are_exact(name, pt):
+@pytest.mark.parametrize("name,pt,g", [("llama13b", 0, 1), ("random", 48, 1), ("random", 16, 1), ("random", 0, 1),
+                                       ("random", 1024, 1), ("random", 0, 4)])
+def test_plan_lists_are_exact(name, pt, g):
     """White-box check of the work-list pre-pass (integer work, bit-exact): the
-    plan at the start of the workspace lists every non-empty partition once, in
+    plan at the start of the workspace lists every non-empty segment once, in
     the documented order."""
     if name == "llama13b":
         wl = synth.make_workload("llama13b")
     else:
-        wl = synth.make_random_workload(4242 + pt, num_seqs=70, num_heads=4, num_kv_heads=2, dtype="fp16",
-                                        max_len=900, min_len=1, groups=3)
+        wl = synth.make_random_workload(4242 + pt + g, num_seqs=70, num_heads=2 * g, num_kv_heads=2,
+                                        dtype="fp16", max_len=900, min_len=1, groups=3)
     step = harness.build_step(wl, partition_tokens=pt)
     desc = step.desc
     S = wl.num_seqs
@@ -237,9 +243,9 @@ def test_plan_lists_are_exact(name, pt):
     ws.fill_(0xAB)
     lens = wl.context_lens.copy()
     ctx = step.context_lens.clone()
-    if name == "random":  # two empty contexts exercise the last class of list B
-        lens[[3, 40]] = 0
-        ctx[[3, 40]] = 0
+    if name != "llama13b":  # two empty contexts exercise the last class of list B
+        lens[[30, 60]] = 0
+        ctx[[30, 60]] = 0
     out = torch.full_like(step.out, 7.0)
     pkv.paged_attn_decode(out, step.q, step.k_cache, step.v_cache, step.block_tables, ctx, wl.scale,
                           wl.num_kv_heads, partition_tokens=pt, workspace=ws)
@@ -248,13 +254,24 @@ def test_plan_lists_are_exact(name, pt):
     plan = ws[: (H0 + S * parts + S) * 4].view(torch.int32).cpu().numpy()
     ref_a, ref_b = _plan_ref(lens, bpp, step.max_blocks)
     F, NB = int(plan[0]), int(plan[1])
-    assert F == len(ref_a) and NB == len(ref_b)
+    assert (F, NB) == (len(ref_a), len(ref_b))
     got_a = [(int(v) & 0xFFFFF, int(v) >> 20) for v in plan[H0:H0 + F]]
     assert got_a == ref_a
     got_b = [int(v) for v in plan[H0 + S * parts:H0 + S * parts + NB]]
     assert got_b == ref_b
-    if name == "random":
-        assert (out[[3, 40]] == 0).all()
+    if name != "llama13b":
+        assert (out[[30, 60]] == 0).all()
+
+
+@pytest.mark.parametrize("g", [1, 2])
+@pytest.mark.parametrize("gs", [2, 4, 5, 9])
+def test_sample_groups_match_oracle(g, gs):
+    """Parallel samples sharing prompt blocks (groups of 2..9 members, cut into
+    work items of at most 4), every output within tolerance."""
+    wl = synth.make_random_workload(7300 + 10 * gs + g, num_seqs=3 * gs + 5, num_heads=3 * g, num_kv_heads=3,
+                                    dtype="fp16", max_len=1400, min_len=1, groups=3, group_size=gs)
+    step = harness.build_step(wl)
+    _check_all(wl, step.out)
 
 
 @pytest.mark.parametrize("g,pt", [(1, 0), (1, 64), (4, 0), (8, 512)])
