@@ -148,11 +148,14 @@ CONFIGS: Dict[str, ConfigSpec] = {
         lengths=("uniform", 1024, 8192), pool_blocks=83223, key_scale=(0.5, 2.0),
         description="GQA decode batch: 256 seqs, 64 query / 8 KV heads, bf16, "
                     "contexts U[1024,8192], per-KV-head key scale U[0.5,2]"),
+    # 512-token partitions: each wave of a decode work-group streams one
+    # 512-token partition of a 2048-token segment; the 4 partitions are merged
+    # in the work-group and the segments by the log-sum-exp reduce kernel
     "long": ConfigSpec(
         name="long", seed=5, num_seqs=8, num_heads=32, num_kv_heads=8, dtype="bf16",
-        lengths=("uniform", 32768, 131072), pool_blocks=46457, partition_tokens=512,
+        lengths=("uniform", 32768, 131072), pool_blocks=46457, partition_tokens=2048,
         description="long-context split decode: 8 seqs, 32 query / 8 KV heads, bf16, "
-                    "contexts U[32768,131072], 512-token partitions"),
+                    "contexts U[32768,131072], 512-token partitions (4 per 2048-token segment)"),
 }
 
 
