@@ -28,10 +28,8 @@ SOURCES = ["api.hip", "decode.hip", "plan.hip", "cache_ops.hip", "block_manager.
 COMMON = ["-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-fgpu-flush-denormals-to-zero", "-munsafe-fp-atomics"]
-# The decode kernels take work items with one atomic per item whose result is
-# consumed only after the item's page loads are issued; the compiler's
-# wave-level atomic rewriting would wait for it at once.
-PER_SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+# Extra flags per source file (none at present).
+PER_SOURCE_FLAGS: dict = {}
 
 
 def hipcc() -> str:

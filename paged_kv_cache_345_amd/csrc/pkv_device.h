@@ -163,12 +163,27 @@ __device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* page) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(page), 0, kPageElems * 2, kBufferDword3);
 }
 typedef int int4_t __attribute__((ext_vector_type(4)));
+// Cache-policy operand of the gfx950 buffer loads: 0 is the default policy,
+// kNonTemporal sets the instruction's nt bit (streaming data, not expected to
+// be reused).
+constexpr int kDefaultPolicy = 0;
+constexpr int kNonTemporal = 2;
 // 16 bytes at lane_off + kConstOff of the descriptor's range (the constant goes
 // to the instruction's immediate offset, the lane part to one VGPR)
-template <int kConstOff>
+template <int kConstOff, int kPolicy = kDefaultPolicy>
 __device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off) {
   return __builtin_bit_cast(uint4,
-                            __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(lane_off), kConstOff, 0));
+                            __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(lane_off), kConstOff, kPolicy));
+}
+
+// Stores through a page descriptor, at a byte offset inside the page.
+template <int kPolicy = kDefaultPolicy>
+__device__ inline void store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int4_t, x), r, static_cast<int>(byte_off), 0, kPolicy);
+}
+template <int kPolicy = kDefaultPolicy>
+__device__ inline void store2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint16_t x) {
+  __builtin_amdgcn_raw_buffer_store_b16(x, r, static_cast<int>(byte_off), 0, kPolicy);
 }
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
