@@ -484,69 +484,39 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
 // Log-sum-exp merge of segment partials: one work-group per (seq, head).
 //   M = max_p m_p,  c_p = 2^(m_p - M),  out = sum_p c_p O_p / sum_p c_p Z_p
 // ---------------------------------------------------------------------------
+// One wave per (sequence, head) row with more than one segment; 4 rows per
+// work-group.  The segments' (m, Z) are wave-uniform loads; lane l merges
+// output dims 2l and 2l+1 over the segments:
+//   M = max_p m_p,  c_p = 2^(m_p - M),  out = sum_p c_p O_p / sum_p c_p Z_p.
 template <class DT>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-  __shared__ float wts[kMaxPartitions];
-  __shared__ float red[8 * kHeadSize];
-  __shared__ float scal[8];
-  const int tid = threadIdx.x;
-  const int s = blockIdx.x / a.num_heads;
-  const int h = blockIdx.x - s * a.num_heads;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave_id_uniform();
+  if (row >= static_cast<int64_t>(a.num_seqs) * a.num_heads) return;
+  const int s = static_cast<int>(row / a.num_heads);
+  const int lane = threadIdx.x & (kWave - 1);
   const int L = clamped_len(a, s);
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
   const int n = (nblk + a.blocks_per_part - 1) / a.blocks_per_part;
   if (n <= 1) return;  // written directly by the decode kernel
-  const int64_t base = (static_cast<int64_t>(s) * a.num_heads + h) * a.parts_max;
+  const int64_t base = row * a.parts_max;
   const float* ml = a.ws_ml + 2 * base;
 
   float mx = -__builtin_inff();
-  for (int p = tid; p < n; p += 256) mx = fmaxf(mx, ml[2 * p]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-  if ((tid & 63) == 0) scal[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(scal[0], scal[1]), fmaxf(scal[2], scal[3]));
-
-  float zs = 0.f;
-  for (int p = tid; p < n; p += 256) {
-    const float w = exp2_fast(ml[2 * p] - mx);
-    wts[p] = w;
-    zs += w * ml[2 * p + 1];
-  }
-  zs += __shfl_xor(zs, 32, 64);
-  zs += __shfl_xor(zs, 16, 64);
-  zs += __shfl_xor(zs, 8, 64);
-  zs += __shfl_xor(zs, 4, 64);
-  zs += __shfl_xor(zs, 2, 64);
-  zs += __shfl_xor(zs, 1, 64);
-  if ((tid & 63) == 0) scal[4 + (tid >> 6)] = zs;
-  __syncthreads();
-  const float Z = (scal[4] + scal[5]) + (scal[6] + scal[7]);
-
-  // thread -> (segment group pg of 8, dims 4*dl .. 4*dl+3)
-  const int pg = tid >> 5;
-  const int dl = tid & 31;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p = pg; p < n; p += 8) {
-    const float w = wts[p];
-    const float4 o = reinterpret_cast<const float4*>(a.ws_o + (base + p) * kHeadSize)[dl];
-    acc.x = fmaf(w, o.x, acc.x);
-    acc.y = fmaf(w, o.y, acc.y);
-    acc.z = fmaf(w, o.z, acc.z);
-    acc.w = fmaf(w, o.w, acc.w);
-  }
-  reinterpret_cast<float4*>(red + pg * kHeadSize)[dl] = acc;
-  __syncthreads();
-  if (tid < kHeadSize) {
-    float t = 0.f;
+  for (int p = lane; p < n; p += kWave) mx = fmaxf(mx, ml[2 * p]);
 #pragma unroll
-    for (int gg = 0; gg < 8; ++gg) t += red[gg * kHeadSize + tid];
-    a.out[(static_cast<int64_t>(s) * a.num_heads + h) * kHeadSize + tid] = DT::from_f32(t / Z);
+  for (int d = kWave / 2; d > 0; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+
+  const float2* o = reinterpret_cast<const float2*>(a.ws_o + base * kHeadSize) + lane;
+  float z = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
+  for (int p = 0; p < n; ++p) {
+    const float c = exp2_fast(ml[2 * p] - mx);
+    const float2 v = o[p * (kHeadSize / 2)];
+    z = fmaf(c, ml[2 * p + 1], z);
+    o0 = fmaf(c, v.x, o0);
+    o1 = fmaf(c, v.y, o1);
   }
+  reinterpret_cast<uint32_t*>(a.out + row * kHeadSize)[lane] = DT::pack2(o0 / z, o1 / z);
 }
 
 template <class DT>
@@ -560,7 +530,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.parts_max > 1) {
-    const int64_t rgrid = static_cast<int64_t>(a.num_seqs) * a.num_heads;
+    const int64_t rgrid = (static_cast<int64_t>(a.num_seqs) * a.num_heads + kWavesPerGroup - 1) / kWavesPerGroup;
     decode_reduce_kernel<DT><<<dim3(static_cast<uint32_t>(rgrid)), dim3(256), 0, stream>>>(a);
     err = hipGetLastError();
   }
