@@ -37,19 +37,23 @@ int64_t resident_work_groups(int32_t group, int32_t dtype) {
 }
 
 // Segment length in blocks.  Automatic choice: the largest power of two in
-// [16, 128] blocks that is at most the expected work per resident work-group
-// (rows x max_blocks / 2 over the resident work-groups), so the longest items,
-// which run first, never outlast the rest; at least 16 blocks (4 per wave);
-// doubled (up to 256) only if the segment count would exceed the reduce
-// kernel's bound.  The choice depends on the shapes only, never on the GPU.
+// [16, 256] blocks that is at most the work of one resident work-group at the
+// row bound (rows x max_blocks over the resident work-groups) and at most the
+// smallest power of two covering max_blocks; doubled (up to 256) only if the
+// segment count would exceed the reduce kernel's bound.  Longer segments mean
+// fewer partials to merge; measured on MI355X, this bound keeps the work
+// balanced while removing most of the merge (GQA batch 3%, LLaMA-7B batch 3%
+// faster than half as long).  The choice depends on the shapes only.
 pkv_status resolve_partition(int32_t num_seqs, int32_t units, int32_t group, int32_t dtype, int32_t max_blocks_per_seq,
                              int32_t partition_tokens, int32_t* bpp_out, int32_t* parts_out) {
   int32_t bpp;
   if (partition_tokens == 0) {
     const int64_t rows = static_cast<int64_t>(num_seqs) * units;
-    const int64_t per_wg = rows * max_blocks_per_seq / (2 * resident_work_groups(group, dtype));
+    const int64_t per_wg = rows * max_blocks_per_seq / resident_work_groups(group, dtype);
+    int32_t cover = 16;
+    while (cover < max_blocks_per_seq && cover < pkv::kMaxSegmentBlocks) cover *= 2;
     bpp = 16;
-    while (bpp < 128 && 2 * bpp <= per_wg) bpp *= 2;
+    while (bpp < cover && 2 * bpp <= per_wg) bpp *= 2;
     while ((max_blocks_per_seq + bpp - 1) / bpp > pkv::kMaxPartitions && bpp < pkv::kMaxSegmentBlocks) bpp *= 2;
   } else {
     if (partition_tokens < pkv::kBlockSize || partition_tokens % pkv::kBlockSize != 0 ||

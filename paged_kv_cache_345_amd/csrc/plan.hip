@@ -46,11 +46,6 @@ __device__ inline int class_of(int r, int bpp) {
   const int nb = num_classes(bpp) - 1;
   return r ? ((bpp - 1 - r) * nb) / (bpp - 1) : nb;
 }
-__device__ inline bool in_class(int fr, int c, int bpp) {
-  const int r = fr & ((1 << kRBits) - 1);
-  const int f = fr >> kRBits;
-  return (r || f == 0) && class_of(r, bpp) == c;
-}
 
 // Exclusive prefix sum of x[0..n) in place, by one wave; returns the total.
 __device__ int wave_exclusive_scan(int* x, int n, int lane) {
@@ -77,6 +72,7 @@ __device__ int wave_exclusive_scan(int* x, int n, int lane) {
 
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(PlanArgs a) {
   __shared__ int fr[kPlanMaxSeqs];            // f << kRBits | r per sequence
+  __shared__ int8_t cls[kPlanMaxSeqs];        // list B class per sequence, -1 if none
   __shared__ int hist_f[kMaxPartitions + 2];  // count of f, then prefix data
   __shared__ int cnt[kPlanMaxTasks];          // per (segment | class, chunk) counts
   __shared__ int cls_off[kPlanClasses + 1];   // partial classes, size descending
@@ -93,23 +89,36 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(PlanArgs a) {
   int* list_a = a.plan + kPlanHeaderInts;
   int* list_b = list_a + static_cast<int64_t>(S) * a.parts_max;
 
+  // the context lengths are the kernel's longest wait: load them first
+  constexpr int kSeqsPerThread = kPlanMaxSeqs / kPlanThreads;
+  int lens[kSeqsPerThread];
+#pragma unroll
+  for (int k = 0; k < kSeqsPerThread; ++k) {
+    const int s = tid + k * kPlanThreads;
+    lens[k] = s < S ? a.context_lens[s] : 0;
+  }
   for (int i = tid; i <= a.parts_max + 1; i += kPlanThreads) hist_f[i] = 0;
   for (int i = tid; i <= kPlanClasses; i += kPlanThreads) cls_off[i] = 0;
   if (tid == 0) f_max = 0;
 
   __syncthreads();
 
-  // per-sequence segment counts
-  for (int s = tid; s < S; s += kPlanThreads) {
-    int L = a.context_lens[s];
-    L = L < 0 ? 0 : L;
-    const int nblk = min((L + kBlockSize - 1) / kBlockSize, cap);
-    const int f = nblk / bpp;
-    const int r = nblk - f * bpp;
-    fr[s] = (f << kRBits) | r;
-    atomicAdd(&hist_f[f], 1);
-    if (r || nblk == 0) atomicAdd(&cls_off[class_of(r, bpp)], 1);
-    atomicMax(&f_max, f);
+  // per-sequence segment counts and list B class
+#pragma unroll
+  for (int k = 0; k < kSeqsPerThread; ++k) {
+    const int s = tid + k * kPlanThreads;
+    if (s < S) {
+      const int L = lens[k] < 0 ? 0 : lens[k];
+      const int nblk = min((L + kBlockSize - 1) / kBlockSize, cap);
+      const int f = nblk / bpp;
+      const int r = nblk - f * bpp;
+      fr[s] = (f << kRBits) | r;
+      const int c = (r || nblk == 0) ? class_of(r, bpp) : -1;
+      cls[s] = static_cast<int8_t>(c);
+      atomicAdd(&hist_f[f], 1);
+      if (c >= 0) atomicAdd(&cls_off[c], 1);
+      atomicMax(&f_max, f);
+    }
   }
   __syncthreads();
 
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(PlanArgs a) {
     const int key = t / nch;
     const int s = chunk * kWave + lane;
     bool pred = false;
-    if (s < S) pred = t < ta ? (fr[s] >> kRBits) > key : in_class(fr[s], key - P, bpp);
+    if (s < S) pred = t < ta ? (fr[s] >> kRBits) > key : cls[s] == key - P;
     const uint64_t m = __ballot(pred);
     if (lane == 0) cnt[t] = __popcll(m);
   }
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(PlanArgs a) {
     const int key = t / nch;
     const int s = chunk * kWave + lane;
     bool pred = false;
-    if (s < S) pred = t < ta ? (fr[s] >> kRBits) > key : in_class(fr[s], key - P, bpp);
+    if (s < S) pred = t < ta ? (fr[s] >> kRBits) > key : cls[s] == key - P;
     const uint64_t m = __ballot(pred);
     const int rank = __popcll(m & ((uint64_t{1} << lane) - 1));
     if (pred) {

@@ -141,13 +141,16 @@ def test_workspace_and_partitions():
 
 @pytest.mark.parametrize("S,Hq,Hkv,dt,mb,expect", [
     (128, 40, 40, pkv.PKV_F16, 128, 2048),  # LLaMA-13B-shaped: one segment per row
-    (64, 32, 32, pkv.PKV_F16, 128, 1024),   # LLaMA-7B-shaped: fewer rows, shorter segments
-    (256, 64, 8, pkv.PKV_BF16, 511, 2048),  # GQA batch
+    (64, 32, 32, pkv.PKV_F16, 128, 2048),   # LLaMA-7B-shaped: one segment per row
+    (64, 32, 32, pkv.PKV_F16, 512, 4096),   # same rows, 4x the table: the 256-block cap
+    (16, 32, 32, pkv.PKV_F16, 128, 512),    # few rows: shorter segments
+    (256, 64, 8, pkv.PKV_BF16, 511, 4096),  # GQA batch
     (4, 8, 8, pkv.PKV_F16, 16, 256),        # tiny batch
 ])
 def test_automatic_segment_length(S, Hq, Hkv, dt, mb, expect):
-    """Segments are a power of two in [16, 128] blocks sized so that one item
-    is at most the expected work of a resident work-group (shapes only)."""
+    """Segments are a power of two in [16, 256] blocks, at most the work of
+    one resident work-group at the row bound and at most the power of two
+    covering the table (shapes only)."""
     d = pkv.CacheDesc(100000, 16, Hkv, 128, dt)
     assert pkv.partition_tokens_for(S, Hq, mb, d) == expect
 
