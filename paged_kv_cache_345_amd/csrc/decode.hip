@@ -485,9 +485,12 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
 //   M = max_p m_p,  c_p = 2^(m_p - M),  out = sum_p c_p O_p / sum_p c_p Z_p
 // ---------------------------------------------------------------------------
 // One wave per (sequence, head) row with more than one segment; 4 rows per
-// work-group.  The segments' (m, Z) are wave-uniform loads; lane l merges
-// output dims 2l and 2l+1 over the segments:
+// work-group:
 //   M = max_p m_p,  c_p = 2^(m_p - M),  out = sum_p c_p O_p / sum_p c_p Z_p.
+// Up to 4 segments, lane l merges output dims 2l and 2l+1 over all of them.
+// Longer rows: lane l = 16 sg + dg takes the segments p = sg (mod 4) for dims
+// 8 dg .. 8 dg + 7, so 4 segments are in flight per step, and the 4 segment
+// groups are summed across the wave at the end.
 template <class DT>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave_id_uniform();
@@ -506,17 +509,53 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 #pragma unroll
   for (int d = kWave / 2; d > 0; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
 
-  const float2* o = reinterpret_cast<const float2*>(a.ws_o + base * kHeadSize) + lane;
-  float z = 0.f, o0 = 0.f, o1 = 0.f;
-#pragma unroll 4
-  for (int p = 0; p < n; ++p) {
-    const float c = exp2_fast(ml[2 * p] - mx);
-    const float2 v = o[p * (kHeadSize / 2)];
-    z = fmaf(c, ml[2 * p + 1], z);
-    o0 = fmaf(c, v.x, o0);
-    o1 = fmaf(c, v.y, o1);
+  if (n <= 4) {
+    const float2* o = reinterpret_cast<const float2*>(a.ws_o + base * kHeadSize) + lane;
+    float z = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int p = 0; p < n; ++p) {
+      const float c = exp2_fast(ml[2 * p] - mx);
+      const float2 v = o[p * (kHeadSize / 2)];
+      z = fmaf(c, ml[2 * p + 1], z);
+      o0 = fmaf(c, v.x, o0);
+      o1 = fmaf(c, v.y, o1);
+    }
+    reinterpret_cast<uint32_t*>(a.out + row * kHeadSize)[lane] = DT::pack2(o0 / z, o1 / z);
+    return;
   }
-  reinterpret_cast<uint32_t*>(a.out + row * kHeadSize)[lane] = DT::pack2(o0 / z, o1 / z);
+
+  const int sg = lane >> 4;
+  const int dg = lane & 15;
+  float z = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll 2
+  for (int p = sg; p < n; p += 4) {
+    const float c = exp2_fast(ml[2 * p] - mx);
+    const float4* o = reinterpret_cast<const float4*>(a.ws_o + (base + p) * kHeadSize) + 2 * dg;
+    const float4 v0 = o[0];
+    const float4 v1 = o[1];
+    z = fmaf(c, ml[2 * p + 1], z);
+    acc[0] = fmaf(c, v0.x, acc[0]);
+    acc[1] = fmaf(c, v0.y, acc[1]);
+    acc[2] = fmaf(c, v0.z, acc[2]);
+    acc[3] = fmaf(c, v0.w, acc[3]);
+    acc[4] = fmaf(c, v1.x, acc[4]);
+    acc[5] = fmaf(c, v1.y, acc[5]);
+    acc[6] = fmaf(c, v1.z, acc[6]);
+    acc[7] = fmaf(c, v1.w, acc[7]);
+  }
+  z = cross_row_sum(z);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = cross_row_sum(acc[i]);
+  if (sg == 0) {
+    uint4 packed;
+    packed.x = DT::pack2(acc[0] / z, acc[1] / z);
+    packed.y = DT::pack2(acc[2] / z, acc[3] / z);
+    packed.z = DT::pack2(acc[4] / z, acc[5] / z);
+    packed.w = DT::pack2(acc[6] / z, acc[7] / z);
+    reinterpret_cast<uint4*>(a.out + row * kHeadSize)[dg] = packed;
+  }
 }
 
 template <class DT>
