@@ -25,6 +25,9 @@ What it computes, in float64 from the same fp16/bf16 values the GPU reads:
   per-sequence K/V, independent of everything above.
 * ``partition_partials_ref`` / ``lse_merge_ref`` — the same softmax split into
   token partitions and recombined by the log-sum-exp identity.
+* ``fp8`` — the fp8 (E4M3) KV cache variant: the E4M3 codec written from its
+  definition, the quantising slot-mapped write and decode attention over the
+  dequantised rows (readings stated in ``oracle/fp8.py``).
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 closed forms, special cases, brute force and the facts the pages print (see the
@@ -42,6 +45,7 @@ from .attention import (
     lse_merge_ref,
 )
 from .runner import OracleStep, run_decode_step
+from . import fp8
 
 __all__ = [
     "to_f64",
@@ -57,4 +61,5 @@ __all__ = [
     "lse_merge_ref",
     "OracleStep",
     "run_decode_step",
+    "fp8",
 ]

@@ -32,7 +32,7 @@ from __future__ import annotations
 import math
 import os
 from concurrent.futures import ThreadPoolExecutor
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -117,6 +117,9 @@ class ConfigSpec:
     key_scale: Optional[Tuple[float, float]] = None  # per-KV-head U[lo, hi] key scale
     partition_tokens: int = 0  # 0: library default
     description: str = ""
+    kv_dtype: Optional[str] = None  # "fp8e4m3": the cache stores E4M3 codes of the rows
+    k_scale: float = 1.0  # fp8 cache: dequantised K = code value * k_scale
+    v_scale: float = 1.0
 
     @property
     def group_size(self) -> int:
@@ -157,6 +160,19 @@ CONFIGS: Dict[str, ConfigSpec] = {
         description="long-context split decode: 8 seqs, 32 query / 8 KV heads, bf16, "
                     "contexts U[32768,131072], 512-token partitions (4 per 2048-token segment)"),
 }
+
+# fp8 (E4M3) cache variants of two batches: same lengths, pools and values;
+# the cache holds E4M3 codes of the rows under one float32 scale per cache
+# (max |row| / scale stays near the E4M3 limit of 448 for N(0,1) rows)
+CONFIGS["llama13b_fp8"] = replace(
+    CONFIGS["llama13b"], name="llama13b_fp8", kv_dtype="fp8e4m3", k_scale=0.0125, v_scale=0.0125,
+    description="LLaMA-13B-shaped decode batch over an fp8 (E4M3) cache: 128 seqs, 40 MHA heads, "
+                "fp16 queries, lognormal contexts (median 600, cap 2048), 13 groups of 3 parallel "
+                "samples, K/V scales 0.0125")
+CONFIGS["gqa_fp8"] = replace(
+    CONFIGS["gqa"], name="gqa_fp8", kv_dtype="fp8e4m3", k_scale=0.025, v_scale=0.0125,
+    description="GQA decode batch over an fp8 (E4M3) cache: 256 seqs, 64 query / 8 KV heads, bf16 "
+                "queries, contexts U[1024,8192], per-KV-head key scale U[0.5,2], K scale 0.025, V scale 0.0125")
 
 
 # --------------------------------------------------------------------------
@@ -199,6 +215,19 @@ class Workload:
     @property
     def dtype(self) -> str:
         return self.spec.dtype
+
+    @property
+    def kv_dtype(self) -> str:
+        """Storage type of the cache: the activation dtype, or "fp8e4m3"."""
+        return self.spec.kv_dtype or self.spec.dtype
+
+    @property
+    def k_scale(self) -> float:
+        return self.spec.k_scale
+
+    @property
+    def v_scale(self) -> float:
+        return self.spec.v_scale
 
     @property
     def pool_blocks(self) -> int:
@@ -339,7 +368,8 @@ def make_workload(name_or_spec, *, with_q: bool = True) -> Workload:
 def make_random_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_heads: int,
                          dtype: str, max_len: int, pool_slack: int = 4,
                          min_len: int = 1, groups: int = 0, group_size: int = 3,
-                         key_scale=None) -> Workload:
+                         key_scale=None, kv_dtype: Optional[str] = None, k_scale: float = 1.0,
+                         v_scale: float = 1.0) -> Workload:
     """Small random workload for property tests: lengths U[min_len, max_len],
     optionally the first group_size*groups sequences in sampling groups of
     group_size."""
@@ -356,7 +386,7 @@ def make_random_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_hea
     spec = ConfigSpec(name=f"random{seed}", seed=seed, num_seqs=num_seqs, num_heads=num_heads,
                       num_kv_heads=num_kv_heads, dtype=dtype,
                       lengths=("fixed", tuple(int(v) for v in lens)), pool_blocks=pool,
-                      key_scale=key_scale)
+                      key_scale=key_scale, kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
     free_order = rng.permutation(pool).astype(np.int32)
     key_scales = None
     if key_scale is not None:
