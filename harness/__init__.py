@@ -66,25 +66,32 @@ class GpuStep:
     def desc(self):
         return pkv.cache_desc(self.wl.pool_blocks, self.wl.num_kv_heads, self.k_cache.dtype)
 
+    @property
+    def fp8(self) -> bool:
+        return self.wl.kv_dtype == "fp8e4m3"
+
     # the three GPU calls of one decode step
     def copy(self, stream=None):
         if self.block_pairs_host.shape[0]:
             pkv.copy_blocks(self.k_cache, self.v_cache, self.block_pairs, stream=stream)
 
     def write(self, stream=None):
-        pkv.reshape_and_cache(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slot_mapping, stream=stream)
+        write_rows(self.wl, self.k_new, self.v_new, self.k_cache, self.v_cache, self.slot_mapping, stream=stream)
 
     def decode(self, out=None, stream=None, partition_tokens=None, block_tables=None, k_cache=None,
                v_cache=None, q=None):
         pt = self.partition_tokens if partition_tokens is None else partition_tokens
         out = self.out if out is None else out
         ws = self.workspace if pt == self.partition_tokens else None
-        pkv.paged_attn_decode(out, self.q if q is None else q,
-                              self.k_cache if k_cache is None else k_cache,
-                              self.v_cache if v_cache is None else v_cache,
-                              self.block_tables if block_tables is None else block_tables,
-                              self.context_lens, self.wl.scale, self.wl.num_kv_heads,
-                              partition_tokens=pt, workspace=ws, stream=stream)
+        args = (out, self.q if q is None else q, self.k_cache if k_cache is None else k_cache,
+                self.v_cache if v_cache is None else v_cache,
+                self.block_tables if block_tables is None else block_tables,
+                self.context_lens, self.wl.scale, self.wl.num_kv_heads)
+        if self.fp8:
+            pkv.paged_attn_decode_fp8(*args, self.wl.k_scale, self.wl.v_scale, partition_tokens=pt, workspace=ws,
+                                      stream=stream)
+        else:
+            pkv.paged_attn_decode(*args, partition_tokens=pt, workspace=ws, stream=stream)
         return out
 
     def plan(self, stream=None):
@@ -93,11 +100,16 @@ class GpuStep:
                                    self.workspace, partition_tokens=self.partition_tokens, stream=stream)
 
     def run(self, out=None, stream=None):
-        """Attention from the planned work list (paged_attn_decode_run)."""
+        """Attention from the planned work list (paged_attn_decode_run[_fp8])."""
         out = self.out if out is None else out
-        pkv.paged_attn_decode_run(out, self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
-                                  self.wl.scale, self.wl.num_kv_heads, workspace=self.workspace,
-                                  partition_tokens=self.partition_tokens, stream=stream)
+        args = (out, self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens, self.wl.scale,
+                self.wl.num_kv_heads)
+        if self.fp8:
+            pkv.paged_attn_decode_run_fp8(*args, self.wl.k_scale, self.wl.v_scale, workspace=self.workspace,
+                                          partition_tokens=self.partition_tokens, stream=stream)
+        else:
+            pkv.paged_attn_decode_run(*args, workspace=self.workspace, partition_tokens=self.partition_tokens,
+                                      stream=stream)
         return out
 
     def run_step(self, stream=None):
@@ -106,15 +118,23 @@ class GpuStep:
         return self.decode(stream=stream)
 
 
-def _flush(chunks, k_cache, v_cache, dtype, device):
+def write_rows(wl, k, v, k_cache, v_cache, slot_mapping, stream=None):
+    """reshape_and_cache, or reshape_and_cache_fp8 with the workload's scales."""
+    if wl.kv_dtype == "fp8e4m3":
+        pkv.reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, wl.k_scale, wl.v_scale, stream=stream)
+    else:
+        pkv.reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, stream=stream)
+
+
+def _flush(wl, chunks, k_cache, v_cache, dtype, device):
     import torch
     if not chunks:
         return
     slots = np.concatenate([c[0] for c in chunks]).astype(np.int32)
     k = np.concatenate([c[1] for c in chunks])
     v = np.concatenate([c[2] for c in chunks])
-    pkv.reshape_and_cache(to_device(k, dtype, device), to_device(v, dtype, device), k_cache, v_cache,
-                          torch.from_numpy(slots).to(device))
+    write_rows(wl, to_device(k, dtype, device), to_device(v, dtype, device), k_cache, v_cache,
+               torch.from_numpy(slots).to(device))
     chunks.clear()
 
 
@@ -126,25 +146,31 @@ def build_step(wl: synth.Workload, device="cuda", *, garbage: str = "nan", garba
 
     The never-written slots start as ``garbage``: "nan" (all-ones bits),
     "random" (seeded bits), "none" (uninitialised), or "pages" with
-    ``initial_pages`` = (K, V) uint16 bit arrays [NB, Hkv, 2048]."""
+    ``initial_pages`` = (K, V) uint16 (uint8 for an fp8 cache) bit arrays
+    [NB, Hkv, 2048].  An fp8 workload (``wl.kv_dtype == "fp8e4m3"``) gets
+    uint8 caches written and read through the ``*_fp8`` calls."""
     import torch
 
     dtype = wl.dtype
     tdt = torch_dtype(dtype)
     hkv = wl.num_kv_heads
-    k_cache, v_cache = pkv.allocate_cache(wl.pool_blocks, hkv, tdt, device)
-    if garbage == "nan":  # all-ones bits: NaN in fp16 and bf16
-        k_cache.view(torch.int16).fill_(-1)
-        v_cache.view(torch.int16).fill_(-1)
+    fp8 = wl.kv_dtype == "fp8e4m3"
+    cdt = torch.uint8 if fp8 else tdt
+    k_cache, v_cache = pkv.allocate_cache(wl.pool_blocks, hkv, cdt, device)
+    bits = torch.uint8 if fp8 else torch.int16  # the caches' raw element bits
+    if garbage == "nan":  # all-ones bits: NaN in fp16, bf16 and E4M3
+        k_cache.view(bits).fill_(-1 if not fp8 else 255)
+        v_cache.view(bits).fill_(-1 if not fp8 else 255)
     elif garbage == "random":
         g = torch.Generator(device=device)
         g.manual_seed(garbage_seed)
+        lo, hi = (0, 256) if fp8 else (-32768, 32767)
         for c in (k_cache, v_cache):
-            c.view(torch.int16).copy_(torch.randint(-32768, 32767, c.shape, generator=g, device=device,
-                                                    dtype=torch.int16))
+            c.view(bits).copy_(torch.randint(lo, hi, c.shape, generator=g, device=device, dtype=bits))
     elif garbage == "pages":
-        k_cache.view(torch.int16).copy_(torch.from_numpy(initial_pages[0].view(np.int16)).to(device))
-        v_cache.view(torch.int16).copy_(torch.from_numpy(initial_pages[1].view(np.int16)).to(device))
+        view = np.uint8 if fp8 else np.int16
+        k_cache.view(bits).copy_(torch.from_numpy(initial_pages[0].view(view)).to(device))
+        v_cache.view(bits).copy_(torch.from_numpy(initial_pages[1].view(view)).to(device))
     elif garbage != "none":
         raise ValueError(garbage)
 
@@ -171,9 +197,9 @@ def build_step(wl: synth.Workload, device="cuda", *, garbage: str = "nan", garba
             pending.append((slots, k, v))
             pending_tokens += slots.shape[0]
             if pending_tokens >= fill_chunk_tokens:
-                _flush(pending, k_cache, v_cache, dtype, device)
+                _flush(wl, pending, k_cache, v_cache, dtype, device)
                 pending_tokens = 0
-    _flush(pending, k_cache, v_cache, dtype, device)
+    _flush(wl, pending, k_cache, v_cache, dtype, device)
 
     slots, pairs = bm.step(step_seqs)
     S = wl.num_seqs
@@ -181,7 +207,7 @@ def build_step(wl: synth.Workload, device="cuda", *, garbage: str = "nan", garba
         max_blocks = max(bm.num_seq_blocks(s) for s in range(S))
     tables = bm.block_table(range(S), max_blocks)
     k_new, v_new = wl.new_token_kv()
-    desc = pkv.cache_desc(wl.pool_blocks, hkv, tdt)
+    desc = pkv.cache_desc(wl.pool_blocks, hkv, cdt)
     pt = wl.spec.partition_tokens if partition_tokens is None else partition_tokens
     ws_bytes = pkv.workspace_size(S, wl.num_heads, max_blocks, desc, pt)
     step = GpuStep(

@@ -60,7 +60,7 @@ typedef enum {
   PKV_ERR_OUT_OF_BLOCKS = 4  /* block manager: the free list cannot cover the request */
 } pkv_status;
 
-typedef enum { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
+typedef enum { PKV_F16 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 
 /* Shape of one layer's paged KV cache. */
 typedef struct {
@@ -68,15 +68,20 @@ typedef struct {
   int32_t block_size;   /* tokens per block; must be 16 */
   int32_t num_kv_heads; /* Hkv */
   int32_t head_size;    /* must be 128 */
-  int32_t dtype;        /* pkv_dtype of the cache, of q/out and of new k/v */
+  int32_t dtype;        /* pkv_dtype of the cache.  PKV_F16 / PKV_BF16: also the
+                           dtype of q, out and the new k/v rows.  PKV_FP8_E4M3:
+                           see the fp8 section below. */
 } pkv_cache_desc;
 
-/* Bytes of ONE of k_cache / v_cache: num_blocks * num_kv_heads * 2048 * 2.
- * Returns 0 for an invalid or unsupported descriptor. */
+/* Bytes of ONE of k_cache / v_cache: num_blocks * num_kv_heads * 2048 * element
+ * bytes (2, or 1 for PKV_FP8_E4M3).  Returns 0 for an invalid or unsupported
+ * descriptor. */
 size_t pkv_cache_bytes(const pkv_cache_desc* cache);
 
 /* Element offset of (block, head, token, dim) inside k_cache / v_cache, from the
- * layout formulas above.  -1 on out-of-range arguments.  Host-only helpers. */
+ * layout formulas above (the fp8 formulas below for a PKV_FP8_E4M3 cache,
+ * where an element is one byte).  -1 on out-of-range arguments.  Host-only
+ * helpers. */
 int64_t pkv_k_index(const pkv_cache_desc* cache, int32_t block, int32_t head, int32_t token, int32_t dim);
 int64_t pkv_v_index(const pkv_cache_desc* cache, int32_t block, int32_t head, int32_t token, int32_t dim);
 
@@ -194,6 +199,64 @@ pkv_status gather_cache(void* k_out, void* v_out, const void* k_cache, const voi
                         const int32_t* block_tables, const int32_t* context_lens,
                         int32_t num_seqs, int32_t max_blocks_per_seq, const int32_t* out_offsets,
                         const pkv_cache_desc* cache, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * fp8 KV cache ([repo] §三: the KV cache itself can be stored quantised; the
+ * format and the scaling below are this library's reading).
+ *
+ * A PKV_FP8_E4M3 cache stores one byte per element: the OCP 8-bit floating-
+ * point E4M3 code (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent field 0 holds subnormals (m/8) * 2^-6; no infinities; S.1111.111 is
+ * NaN; largest finite magnitude 448).  K and V each have one float32 scale:
+ * the value a K code stands for is E4M3(code) * k_scale, and likewise for V.
+ * Writing x gives the code nearest to the float32 quotient x / scale (one
+ * correctly rounded float32 division), ties to the even mantissa, magnitudes
+ * of 448 and beyond saturated to +-448, the sign of zero kept.  Queries,
+ * outputs and the new k/v rows stay fp16 or bf16 (act_dtype).
+ *
+ * fp8 page layout (byte offsets; page (b, h) starts at byte (b*Hkv + h)*2048):
+ *   K: (d / 64) * 1024 + (16 * ((d / 8) % 4) + t) * 16 + ((d / 32) % 2) * 8 + d % 8
+ *   V: (d / 64) * 1024 + (16 * (t / 4) + d % 16) * 16 + ((d / 32) % 2) * 8
+ *        + ((d / 16) % 2) * 4 + t % 4
+ * A wave reads a page as two contiguous 1 KiB loads; widened to 16 bits, the
+ * 16 bytes a lane receives are its fragments of the 16-bit layout.
+ *
+ * copy_blocks, gather_cache (codes, one byte per element), pkv_cache_bytes,
+ * pkv_k_index / pkv_v_index, paged_attn_decode_plan, _workspace_size and
+ * _partition_tokens accept a PKV_FP8_E4M3 cache as they are.
+ * paged_attn_decode / _run and reshape_and_cache return PKV_ERR_UNSUPPORTED
+ * for it: use the _fp8 entry points, which take the scales.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t act_dtype; /* PKV_F16 or PKV_BF16: dtype of q, out and the new k/v rows */
+  float k_scale;     /* finite and > 0 */
+  float v_scale;     /* finite and > 0 */
+} pkv_fp8_scales;
+
+/* reshape_and_cache into an fp8 cache: the rows (act_dtype) are encoded as
+ * described above.  Arguments and errors otherwise as reshape_and_cache. */
+pkv_status reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                                 const int32_t* slot_mapping, int32_t num_tokens,
+                                 const pkv_cache_desc* cache, const pkv_fp8_scales* scales, void* stream);
+
+/* paged_attn_decode over an fp8 cache: the same attention over the rows'
+ * values E4M3(code) * scale, in fp32 on the GPU; q and out are act_dtype.
+ * Arguments, workspace and errors otherwise as paged_attn_decode; the _run
+ * form pairs with paged_attn_decode_plan as paged_attn_decode_run does. */
+pkv_status paged_attn_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 float scale, int32_t num_kv_heads,
+                                 int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                 const pkv_cache_desc* cache, const pkv_fp8_scales* scales,
+                                 int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+pkv_status paged_attn_decode_run_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     float scale, int32_t num_kv_heads,
+                                     int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                     const pkv_cache_desc* cache, const pkv_fp8_scales* scales,
+                                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 const char* pkv_status_string(pkv_status s);
 const char* pkv_version(void);

@@ -11,7 +11,9 @@ Tensors (PyTorch is used for device memory and streams only):
   k_cache, v_cache [num_blocks, num_kv_heads, 2048]   same dtype, GPU; the page
                    layout inside the last dimension is the library's own (see
                    pagedkv.h); use ``gather_cache`` or ``k_index``/``v_index`` to
-                   read it
+                   read it.  An fp8 (E4M3) cache is a uint8 tensor of codes of
+                   the same shape, used through the ``*_fp8`` calls, which take
+                   the K and V scales
   block_tables    int32 [num_seqs, max_blocks_per_seq], GPU
   context_lens    int32 [num_seqs], GPU
   slot_mapping    int32 [num_tokens], GPU
@@ -39,6 +41,7 @@ PKV_ERR_DEVICE = 3
 PKV_ERR_OUT_OF_BLOCKS = 4
 PKV_F16 = 0
 PKV_BF16 = 1
+PKV_FP8_E4M3 = 2
 
 # Every symbol pagedkv.h declares, with (restype, argtypes).
 _i32 = ctypes.c_int32
@@ -54,7 +57,12 @@ class CacheDesc(ctypes.Structure):
                 ("head_size", _i32), ("dtype", _i32)]
 
 
+class Fp8Scales(ctypes.Structure):
+    _fields_ = [("act_dtype", _i32), ("k_scale", _fl), ("v_scale", _fl)]
+
+
 _DP = ctypes.POINTER(CacheDesc)
+_SP = ctypes.POINTER(Fp8Scales)
 
 SIGNATURES = {
     "pkv_cache_bytes": (_sz, [_DP]),
@@ -68,6 +76,11 @@ SIGNATURES = {
     "paged_attn_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _DP]),
     "paged_attn_decode_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _DP]),
     "reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _DP, _vp]),
+    "reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _DP, _SP, _vp]),
+    "paged_attn_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _SP,
+                                     _i32, _vp, _sz, _vp]),
+    "paged_attn_decode_run_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _SP,
+                                         _i32, _vp, _sz, _vp]),
     "copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _DP, _vp]),
     "gather_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _DP, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -148,12 +161,18 @@ def _torch():
 
 
 def _dtype_code(t) -> int:
+    return _code_of_dtype(t.dtype)
+
+
+def _code_of_dtype(dtype) -> int:
     torch = _torch()
-    if t.dtype == torch.float16:
+    if dtype == torch.float16:
         return PKV_F16
-    if t.dtype == torch.bfloat16:
+    if dtype == torch.bfloat16:
         return PKV_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+    if dtype == torch.uint8:  # a cache of E4M3 codes
+        return PKV_FP8_E4M3
+    raise TypeError(f"unsupported dtype {dtype}; expected float16, bfloat16 or uint8 (fp8 E4M3 codes)")
 
 
 def _gpu(t, name: str, dtype=None, ndim: Optional[int] = None):
@@ -175,9 +194,15 @@ def _stream_handle(stream) -> int:
 
 
 def cache_desc(num_blocks: int, num_kv_heads: int, dtype) -> CacheDesc:
-    torch = _torch()
-    code = dtype if isinstance(dtype, int) else (PKV_F16 if dtype == torch.float16 else PKV_BF16)
+    """dtype: a PKV_* code, or torch.float16 / torch.bfloat16 / torch.uint8 (fp8 E4M3 codes)."""
+    code = dtype if isinstance(dtype, int) else _code_of_dtype(dtype)
     return CacheDesc(int(num_blocks), BLOCK_SIZE, int(num_kv_heads), HEAD_SIZE, code)
+
+
+def fp8_scales(act_dtype, k_scale: float, v_scale: float) -> Fp8Scales:
+    """act_dtype: torch.float16 / torch.bfloat16 (or a PKV_* code) of q, out and the new rows."""
+    code = act_dtype if isinstance(act_dtype, int) else _code_of_dtype(act_dtype)
+    return Fp8Scales(int(code), float(k_scale), float(v_scale))
 
 
 def _desc_of(k_cache) -> CacheDesc:
@@ -230,6 +255,7 @@ def partition_tokens_for(num_seqs: int, num_heads: int, max_blocks_per_seq: int,
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, partition_tokens, workspace):
     torch = _torch()
     desc = _desc_of(k_cache)
+    cache_dtype = torch.uint8 if desc.dtype == PKV_FP8_E4M3 else q.dtype
     if desc.num_kv_heads != num_kv_heads:
         raise ValueError("num_kv_heads does not match the cache")
     num_seqs, num_heads, hs = q.shape
@@ -238,8 +264,8 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_he
     if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs:
         raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
     mbps = int(block_tables.shape[1])
-    ptrs = [_gpu(out, "out", q.dtype, 3), _gpu(q, "q", None, 3), _gpu(k_cache, "k_cache", q.dtype),
-            _gpu(v_cache, "v_cache", q.dtype), _gpu(block_tables, "block_tables", torch.int32, 2),
+    ptrs = [_gpu(out, "out", q.dtype, 3), _gpu(q, "q", None, 3), _gpu(k_cache, "k_cache", cache_dtype),
+            _gpu(v_cache, "v_cache", cache_dtype), _gpu(block_tables, "block_tables", torch.int32, 2),
             _gpu(context_lens, "context_lens", torch.int32, 1)]
     if context_lens.shape[0] != num_seqs or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("context_lens / v_cache shape mismatch")
@@ -290,6 +316,35 @@ def paged_attn_decode_run(out, q, k_cache, v_cache, block_tables, context_lens, 
     return out
 
 
+def paged_attn_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                          num_kv_heads: int, k_scale: float, v_scale: float, *, partition_tokens: int = 0,
+                          workspace=None, stream=None):
+    """paged_attn_decode over an fp8 (E4M3, uint8) cache whose codes stand for
+    code value * k_scale (K) and code value * v_scale (V); q, out fp16/bf16."""
+    ptrs, desc, S, Hq, mbps, ws_ptr, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                                             num_kv_heads, partition_tokens, workspace)
+    sc = fp8_scales(q.dtype, k_scale, v_scale)
+    st = lib().paged_attn_decode_fp8(*ptrs, float(scale), int(num_kv_heads), int(S), int(Hq), mbps,
+                                     ctypes.byref(desc), ctypes.byref(sc), int(partition_tokens), ws_ptr, ws_bytes,
+                                     _stream_handle(stream))
+    _check(st, "paged_attn_decode_fp8")
+    return out
+
+
+def paged_attn_decode_run_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                              num_kv_heads: int, k_scale: float, v_scale: float, *, workspace,
+                              partition_tokens: int = 0, stream=None):
+    """paged_attn_decode_fp8 from a work list written by paged_attn_decode_plan."""
+    ptrs, desc, S, Hq, mbps, ws_ptr, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                                             num_kv_heads, partition_tokens, workspace)
+    sc = fp8_scales(q.dtype, k_scale, v_scale)
+    st = lib().paged_attn_decode_run_fp8(*ptrs, float(scale), int(num_kv_heads), int(S), int(Hq), mbps,
+                                         ctypes.byref(desc), ctypes.byref(sc), int(partition_tokens), ws_ptr,
+                                         ws_bytes, _stream_handle(stream))
+    _check(st, "paged_attn_decode_run_fp8")
+    return out
+
+
 def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, stream=None):
     """Write k[i], v[i] ([num_kv_heads, 128]) of every token i to slot_mapping[i]."""
     torch = _torch()
@@ -302,6 +357,22 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, stream=None):
                                  _gpu(slot_mapping, "slot_mapping", torch.int32, 1), n, ctypes.byref(desc),
                                  _stream_handle(stream))
     _check(st, "reshape_and_cache")
+
+
+def reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, k_scale: float, v_scale: float, *, stream=None):
+    """Write the E4M3 codes of k[i] / k_scale and v[i] / v_scale (fp16/bf16 rows
+    [num_kv_heads, 128]) of every token i to slot_mapping[i] of a uint8 cache."""
+    torch = _torch()
+    desc = _desc_of(k_cache)
+    n = int(slot_mapping.shape[0])
+    if tuple(k.shape) != (n, desc.num_kv_heads, HEAD_SIZE) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k, v must be [num_tokens, num_kv_heads, 128]")
+    sc = fp8_scales(k.dtype, k_scale, v_scale)
+    st = lib().reshape_and_cache_fp8(_gpu(k, "k"), _gpu(v, "v", k.dtype), _gpu(k_cache, "k_cache", torch.uint8),
+                                     _gpu(v_cache, "v_cache", torch.uint8),
+                                     _gpu(slot_mapping, "slot_mapping", torch.int32, 1), n, ctypes.byref(desc),
+                                     ctypes.byref(sc), _stream_handle(stream))
+    _check(st, "reshape_and_cache_fp8")
 
 
 def copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
@@ -433,6 +504,7 @@ __all__ = [
     "LIB_PATH", "BLOCK_SIZE", "HEAD_SIZE", "PAGE_ELEMS", "CacheDesc", "PagedKVError", "OutOfBlocks",
     "lib", "status_string", "version", "cache_desc", "allocate_cache", "k_index", "v_index",
     "workspace_size", "partition_tokens_for", "paged_attn_decode", "paged_attn_decode_plan",
-    "paged_attn_decode_run", "reshape_and_cache", "copy_blocks",
+    "paged_attn_decode_run", "reshape_and_cache", "copy_blocks", "PKV_FP8_E4M3", "Fp8Scales", "fp8_scales",
+    "paged_attn_decode_fp8", "paged_attn_decode_run_fp8", "reshape_and_cache_fp8",
     "gather_cache", "BlockManager", "SIGNATURES",
 ]

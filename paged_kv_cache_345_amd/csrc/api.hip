@@ -19,7 +19,7 @@ constexpr double kLog2e = 1.4426950408889634073599246810019;
 pkv_status check_desc(const pkv_cache_desc* c) {
   if (!c) return PKV_ERR_INVALID;
   if (c->block_size != pkv::kBlockSize || c->head_size != pkv::kHeadSize) return PKV_ERR_UNSUPPORTED;
-  if (c->dtype != PKV_F16 && c->dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (c->dtype != PKV_F16 && c->dtype != PKV_BF16 && c->dtype != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PKV_ERR_INVALID;
   // every page offset must fit int64 comfortably and every slot an int32
   if (static_cast<int64_t>(c->num_blocks) * pkv::kBlockSize > INT32_MAX) return PKV_ERR_INVALID;
@@ -28,9 +28,21 @@ pkv_status check_desc(const pkv_cache_desc* c) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool is_fp8(const pkv_cache_desc* c) { return c->dtype == PKV_FP8_E4M3; }
+int32_t page_bytes(const pkv_cache_desc* c) { return is_fp8(c) ? pkv::kPageBytesFp8 : 2 * pkv::kPageElems; }
+
+// The scales of an fp8 call: act dtype fp16/bf16, finite positive scales.
+pkv_status check_scales(const pkv_fp8_scales* f) {
+  if (!f) return PKV_ERR_INVALID;
+  if (f->act_dtype != PKV_F16 && f->act_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(f->k_scale) || !std::isfinite(f->v_scale) || !(f->k_scale > 0.f) || !(f->v_scale > 0.f))
+    return PKV_ERR_INVALID;
+  return PKV_OK;
+}
+
 // MI355X: 256 compute units; work-groups of the decode kernels that fit on one
 // compute unit at once (4 waves each: MHA fp16 runs 5 waves per SIMD, MHA bf16
-// 4, the GQA kernel 2).
+// and MHA over an fp8 cache 4, the GQA kernels 2).
 constexpr int64_t kComputeUnits = 256;
 int64_t resident_work_groups(int32_t group, int32_t dtype) {
   return kComputeUnits * (group == 1 ? (dtype == PKV_F16 ? 5 : 4) : 2);
@@ -126,21 +138,24 @@ extern "C" {
 
 size_t pkv_cache_bytes(const pkv_cache_desc* cache) {
   if (check_desc(cache) != PKV_OK) return 0;
-  return static_cast<size_t>(cache->num_blocks) * static_cast<size_t>(cache->num_kv_heads) * pkv::kPageElems * 2;
+  return static_cast<size_t>(cache->num_blocks) * static_cast<size_t>(cache->num_kv_heads) *
+         static_cast<size_t>(page_bytes(cache));
 }
 
 int64_t pkv_k_index(const pkv_cache_desc* c, int32_t block, int32_t head, int32_t token, int32_t dim) {
   if (check_desc(c) != PKV_OK || block < 0 || block >= c->num_blocks || head < 0 || head >= c->num_kv_heads ||
       token < 0 || token >= pkv::kBlockSize || dim < 0 || dim >= pkv::kHeadSize)
     return -1;
-  return (static_cast<int64_t>(block) * c->num_kv_heads + head) * pkv::kPageElems + pkv::k_page_offset(token, dim);
+  return (static_cast<int64_t>(block) * c->num_kv_heads + head) * pkv::kPageElems +
+         (is_fp8(c) ? pkv::k_page_offset_fp8(token, dim) : pkv::k_page_offset(token, dim));
 }
 
 int64_t pkv_v_index(const pkv_cache_desc* c, int32_t block, int32_t head, int32_t token, int32_t dim) {
   if (check_desc(c) != PKV_OK || block < 0 || block >= c->num_blocks || head < 0 || head >= c->num_kv_heads ||
       token < 0 || token >= pkv::kBlockSize || dim < 0 || dim >= pkv::kHeadSize)
     return -1;
-  return (static_cast<int64_t>(block) * c->num_kv_heads + head) * pkv::kPageElems + pkv::v_page_offset(token, dim);
+  return (static_cast<int64_t>(block) * c->num_kv_heads + head) * pkv::kPageElems +
+         (is_fp8(c) ? pkv::v_page_offset_fp8(token, dim) : pkv::v_page_offset(token, dim));
 }
 
 int32_t paged_attn_decode_partition_tokens(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
@@ -186,9 +201,17 @@ pkv_status launch_plan(const DecodeLayout& L, const int32_t* context_lens, int32
 pkv_status decode_impl(bool plan_first, void* out, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t num_kv_heads,
                        int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
-                       int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+                       const pkv_fp8_scales* fp8, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   pkv_status st = check_decode_shape(num_seqs, num_heads, max_blocks_per_seq, cache);
   if (st != PKV_OK) return st;
+  // an fp8 cache comes only with its scales, and scales only with an fp8 cache
+  if (is_fp8(cache) != (fp8 != nullptr)) return fp8 ? PKV_ERR_INVALID : PKV_ERR_UNSUPPORTED;
+  if (fp8) {
+    st = check_scales(fp8);
+    if (st != PKV_OK) return st;
+  }
+  const int32_t act_dtype = fp8 ? fp8->act_dtype : cache->dtype;
   if (num_kv_heads != cache->num_kv_heads) return PKV_ERR_INVALID;
   if (!std::isfinite(scale)) return PKV_ERR_INVALID;
   DecodeLayout L;
@@ -211,7 +234,8 @@ pkv_status decode_impl(bool plan_first, void* out, const void* q, const void* k_
   a.ws_o = L.parts > 1 ? reinterpret_cast<float*>(ws + L.partial_o) : nullptr;
   a.ws_ml = L.parts > 1 ? reinterpret_cast<float*>(ws + L.partial_ml) : nullptr;
   a.plan = L.planned ? reinterpret_cast<int*>(ws + L.plan) : nullptr;
-  a.scale_log2e = static_cast<float>(static_cast<double>(scale) * kLog2e);
+  a.scale_log2e = static_cast<float>(static_cast<double>(scale) * kLog2e * (fp8 ? static_cast<double>(fp8->k_scale) : 1.0));
+  a.out_scale = fp8 ? fp8->v_scale : 1.0f;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
@@ -228,7 +252,7 @@ pkv_status decode_impl(bool plan_first, void* out, const void* q, const void* k_
     st = launch_plan(L, context_lens, num_seqs, num_heads, max_blocks_per_seq, workspace, hs);
     if (st != PKV_OK) return st;
   }
-  return from_hip(pkv::launch_decode(a, cache->dtype, hs));
+  return from_hip(pkv::launch_decode(a, act_dtype == PKV_F16 ? 0 : 1, fp8 != nullptr, hs));
 }
 
 }  // namespace
@@ -241,7 +265,31 @@ pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, cons
                              const pkv_cache_desc* cache, int32_t partition_tokens, void* workspace,
                              size_t workspace_bytes, void* stream) {
   return decode_impl(true, out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, num_seqs,
-                     num_heads, max_blocks_per_seq, cache, partition_tokens, workspace, workspace_bytes, stream);
+                     num_heads, max_blocks_per_seq, cache, nullptr, partition_tokens, workspace, workspace_bytes,
+                     stream);
+}
+
+pkv_status paged_attn_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                 int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                 const pkv_cache_desc* cache, const pkv_fp8_scales* scales, int32_t partition_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!scales) return PKV_ERR_INVALID;
+  return decode_impl(true, out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, num_seqs,
+                     num_heads, max_blocks_per_seq, cache, scales, partition_tokens, workspace, workspace_bytes,
+                     stream);
+}
+
+pkv_status paged_attn_decode_run_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                     int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                                     int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                     const pkv_fp8_scales* scales, int32_t partition_tokens, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!scales) return PKV_ERR_INVALID;
+  return decode_impl(false, out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, num_seqs,
+                     num_heads, max_blocks_per_seq, cache, scales, partition_tokens, workspace, workspace_bytes,
+                     stream);
 }
 
 pkv_status paged_attn_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
@@ -264,14 +312,23 @@ pkv_status paged_attn_decode_run(void* out, const void* q, const void* k_cache, 
                                  int32_t max_blocks_per_seq, const pkv_cache_desc* cache, int32_t partition_tokens,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(false, out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, num_seqs,
-                     num_heads, max_blocks_per_seq, cache, partition_tokens, workspace, workspace_bytes, stream);
+                     num_heads, max_blocks_per_seq, cache, nullptr, partition_tokens, workspace, workspace_bytes,
+                     stream);
 }
 
-pkv_status reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
-                             const int32_t* slot_mapping, int32_t num_tokens, const pkv_cache_desc* cache,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+pkv_status write_impl(const void* k, const void* v, void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                      int32_t num_tokens, const pkv_cache_desc* cache, const pkv_fp8_scales* fp8, void* stream) {
   pkv_status st = check_desc(cache);
   if (st != PKV_OK) return st;
+  if (is_fp8(cache) != (fp8 != nullptr)) return fp8 ? PKV_ERR_INVALID : PKV_ERR_UNSUPPORTED;
+  if (fp8) {
+    st = check_scales(fp8);
+    if (st != PKV_OK) return st;
+  }
   if (num_tokens < 0) return PKV_ERR_INVALID;
   if (num_tokens == 0) return PKV_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID;
@@ -281,13 +338,35 @@ pkv_status reshape_and_cache(const void* k, const void* v, void* k_cache, void* 
   for (int32_t t0 = 0; t0 < num_tokens; t0 += chunk) {
     const int32_t n = num_tokens - t0 < chunk ? num_tokens - t0 : chunk;
     const size_t row_off = static_cast<size_t>(t0) * static_cast<size_t>(cache->num_kv_heads) * pkv::kHeadSize;
-    hipError_t e = pkv::launch_reshape_and_cache(static_cast<const uint16_t*>(k) + row_off,
-                                                 static_cast<const uint16_t*>(v) + row_off, k_cache, v_cache,
-                                                 slot_mapping + t0, n, cache->num_kv_heads, cache->num_blocks,
-                                                 static_cast<hipStream_t>(stream));
+    const uint16_t* kt = static_cast<const uint16_t*>(k) + row_off;
+    const uint16_t* vt = static_cast<const uint16_t*>(v) + row_off;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = fp8 ? pkv::launch_reshape_and_cache_fp8(kt, vt, k_cache, v_cache, slot_mapping + t0, n,
+                                                          cache->num_kv_heads, cache->num_blocks,
+                                                          fp8->act_dtype == PKV_F16 ? 0 : 1, fp8->k_scale,
+                                                          fp8->v_scale, hs)
+                       : pkv::launch_reshape_and_cache(kt, vt, k_cache, v_cache, slot_mapping + t0, n,
+                                                      cache->num_kv_heads, cache->num_blocks, hs);
     if (e != hipSuccess) return PKV_ERR_DEVICE;
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                             const int32_t* slot_mapping, int32_t num_tokens, const pkv_cache_desc* cache,
+                             void* stream) {
+  return write_impl(k, v, k_cache, v_cache, slot_mapping, num_tokens, cache, nullptr, stream);
+}
+
+pkv_status reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                                 const int32_t* slot_mapping, int32_t num_tokens, const pkv_cache_desc* cache,
+                                 const pkv_fp8_scales* scales, void* stream) {
+  if (!scales) return PKV_ERR_INVALID;
+  return write_impl(k, v, k_cache, v_cache, slot_mapping, num_tokens, cache, scales, stream);
 }
 
 pkv_status copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
@@ -300,7 +379,7 @@ pkv_status copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID;
   if (static_cast<int64_t>(num_pairs) * 2 * cache->num_kv_heads > INT32_MAX) return PKV_ERR_INVALID;
   return from_hip(pkv::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, cache->num_kv_heads,
-                                          cache->num_blocks, static_cast<hipStream_t>(stream)));
+                                          cache->num_blocks, page_bytes(cache), static_cast<hipStream_t>(stream)));
 }
 
 pkv_status gather_cache(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
@@ -317,7 +396,7 @@ pkv_status gather_cache(void* k_out, void* v_out, const void* k_cache, const voi
   if (static_cast<int64_t>(num_seqs) * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
   return from_hip(pkv::launch_gather_cache(k_out, v_out, k_cache, v_cache, block_tables, context_lens, num_seqs,
                                            max_blocks_per_seq, out_offsets, cache->num_kv_heads, cache->num_blocks,
-                                           static_cast<hipStream_t>(stream)));
+                                           is_fp8(cache), static_cast<hipStream_t>(stream)));
 }
 
 const char* pkv_status_string(pkv_status s) {

@@ -1,5 +1,6 @@
 // Cache data-movement kernels: slot-mapped write, copy-on-write block copy and
-// the paged -> contiguous inspection gather.  All of them move bits only.
+// the paged -> contiguous inspection gather, for 16-bit and fp8 (E4M3) pages.
+// All of them move bits only, except the fp8 write, which encodes.
 //
 // Slot model from page "vLLM 部署与 PagedAttention 原理 · 检索整理（CSDN 频道批次）",
 // item 2: tokens fill fixed-size blocks reached through a block table, and a
@@ -66,15 +67,61 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
-// One work-group of 256 threads copies one 4 KiB page (16 bytes per thread).
-// Work-group index -> (pair, which of the 2*Hkv pages of the block).  The
-// stores are non-temporal: with the default policy the copied lines are still
-// dirty in the memory-side cache when the step's attention kernel runs and
-// slow it by ~4 us on a 128-sequence batch (measured on MI355X); this kernel
-// takes the same time either way.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+// fp8 (E4M3) cache write: the same thread mapping; each element is encoded as
+// e4m3_encode(x / scale) with one correctly rounded float division.  K lands
+// as one 8-byte store (8 consecutive dims of one token are contiguous in the
+// fp8 K page), V as eight 1-byte stores; the K store policy follows the
+// 16-bit kernel above.
+template <class DT>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int64_t num_rows, int num_kv_heads,
+    int64_t num_slots, float k_scale, float v_scale) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = gid >> 4;  // token * Hkv + head
+  const int c = static_cast<int>(gid & 15);
+  if (row >= num_rows) return;
+  const int64_t token = row / num_kv_heads;
+  const int h = static_cast<int>(row - token * num_kv_heads);
+  const int32_t slot = slot_mapping[token];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t block = slot >> 4;
+  const int t = slot & 15;
+  const int64_t num_tokens = num_rows / num_kv_heads;
+  const int32_t prev = token > 0 ? slot_mapping[token - 1] : -1;
+  const int32_t next = token + 1 < num_tokens ? slot_mapping[token + 1] : -1;
+  const bool lone = (prev < 0 || (prev >> 4) != block) && (next < 0 || (next >> 4) != block);
+  const int64_t page = (block * num_kv_heads + h) * kPageBytesFp8;
+
+  const uint4 kv = reinterpret_cast<const uint4*>(k + row * kHeadSize)[c];
+  const uint4 vv = reinterpret_cast<const uint4*>(v + row * kHeadSize)[c];
+  uint2 kq = make_uint2(0u, 0u);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kq.x |= e4m3_encode(elem<DT>(kv, e) / k_scale) << (8 * e);
+    kq.y |= e4m3_encode(elem<DT>(kv, 4 + e) / k_scale) << (8 * e);
+  }
+  const __amdgpu_buffer_rsrc_t kr = range_rsrc(k_cache + page, kPageBytesFp8);
+  if (lone)
+    store8<kNonTemporal>(kr, k_page_offset_fp8(t, 8 * c), kq);
+  else
+    store8(kr, k_page_offset_fp8(t, 8 * c), kq);
+
+  const __amdgpu_buffer_rsrc_t vr = range_rsrc(v_cache + page, kPageBytesFp8);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    store1(vr, v_page_offset_fp8(t, 8 * c + e), static_cast<uint8_t>(e4m3_encode(elem<DT>(vv, e) / v_scale)));
+}
+
+// One work-group copies one page, 16 bytes per thread (256 threads for a
+// 4 KiB 16-bit page, 128 for a 2 KiB fp8 page).  Work-group index -> (pair,
+// which of the 2*Hkv pages of the block).  The stores are non-temporal: with
+// the default policy the copied lines are still dirty in the memory-side cache
+// when the step's attention kernel runs and slow it by ~4 us on a 128-sequence
+// batch (measured on MI355X); this kernel takes the same time either way.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
                                                           const int32_t* __restrict__ block_pairs, int num_kv_heads,
-                                                          int32_t num_blocks) {
+                                                          int32_t num_blocks, int page_bytes) {
   const int64_t wg = blockIdx.x;
   const int pages = 2 * num_kv_heads;
   const int64_t pair = wg / pages;
@@ -82,11 +129,11 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t* __restrict__
   const int32_t src = block_pairs[2 * pair];
   const int32_t dst = block_pairs[2 * pair + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  uint16_t* base = page < num_kv_heads ? k_cache : v_cache;
+  char* base = page < num_kv_heads ? k_cache : v_cache;
   const int h = page < num_kv_heads ? page : page - num_kv_heads;
-  const uint4* s = reinterpret_cast<const uint4*>(base + (static_cast<int64_t>(src) * num_kv_heads + h) * kPageElems);
-  uint16_t* d = base + (static_cast<int64_t>(dst) * num_kv_heads + h) * kPageElems;
-  store16<kNonTemporal>(page_rsrc(d), 16u * threadIdx.x, s[threadIdx.x]);
+  const uint4* s = reinterpret_cast<const uint4*>(base + (static_cast<int64_t>(src) * num_kv_heads + h) * page_bytes);
+  char* d = base + (static_cast<int64_t>(dst) * num_kv_heads + h) * page_bytes;
+  store16<kNonTemporal>(range_rsrc(d, page_bytes), 16u * threadIdx.x, s[threadIdx.x]);
 }
 
 // One work-group per (sequence, logical block).  Thread -> (token, head, chunk).
@@ -128,6 +175,43 @@ __global__ __launch_bounds__(256) void gather_cache_kernel(
   }
 }
 
+// fp8 pages -> contiguous rows of codes (one byte per element).
+__global__ __launch_bounds__(256) void gather_cache_fp8_kernel(
+    uint8_t* __restrict__ k_out, uint8_t* __restrict__ v_out, const uint8_t* __restrict__ k_cache,
+    const uint8_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ out_offsets, int max_blocks_per_seq,
+    int num_kv_heads, int32_t num_blocks) {
+  const int64_t wg = blockIdx.x;
+  const int64_t s = wg / max_blocks_per_seq;
+  const int j = static_cast<int>(wg - s * max_blocks_per_seq);
+  int64_t L = context_lens[s];
+  if (L > static_cast<int64_t>(max_blocks_per_seq) * kBlockSize) L = static_cast<int64_t>(max_blocks_per_seq) * kBlockSize;
+  const int64_t first = static_cast<int64_t>(j) * kBlockSize;
+  if (first >= L) return;
+  const int32_t block = block_tables[s * max_blocks_per_seq + j];
+  if (block < 0 || block >= num_blocks) return;
+  const int ntok = static_cast<int>(L - first < kBlockSize ? L - first : kBlockSize);
+  const int64_t row0 = static_cast<int64_t>(out_offsets[s]) + first;
+  const int work = kBlockSize * num_kv_heads * 16;
+  for (int idx = threadIdx.x; idx < work; idx += blockDim.x) {
+    const int c = idx & 15;
+    const int t = (idx >> 4) & 15;
+    const int h = idx >> 8;
+    if (t >= ntok) continue;
+    const int64_t page = (static_cast<int64_t>(block) * num_kv_heads + h) * kPageBytesFp8;
+    const int64_t out_row = (row0 + t) * num_kv_heads + h;
+    reinterpret_cast<uint2*>(k_out + out_row * kHeadSize)[c] =
+        *reinterpret_cast<const uint2*>(k_cache + page + k_page_offset_fp8(t, 8 * c));
+    uint2 packed = make_uint2(0u, 0u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      packed.x |= static_cast<uint32_t>(v_cache[page + v_page_offset_fp8(t, 8 * c + e)]) << (8 * e);
+      packed.y |= static_cast<uint32_t>(v_cache[page + v_page_offset_fp8(t, 8 * c + 4 + e)]) << (8 * e);
+    }
+    reinterpret_cast<uint2*>(v_out + out_row * kHeadSize)[c] = packed;
+  }
+}
+
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                                     int32_t num_blocks, hipStream_t stream) {
@@ -140,23 +224,50 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
   return hipGetLastError();
 }
 
+hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                                        const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t num_blocks, int act_dtype, float k_scale, float v_scale,
+                                        hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(num_tokens) * num_kv_heads;
+  const int64_t grid = (rows * 16 + 255) / 256;
+  const dim3 g(static_cast<uint32_t>(grid)), b(256);
+  auto* kk = static_cast<const uint16_t*>(k);
+  auto* vv = static_cast<const uint16_t*>(v);
+  auto* kc = static_cast<uint8_t*>(k_cache);
+  auto* vc = static_cast<uint8_t*>(v_cache);
+  const int64_t slots = static_cast<int64_t>(num_blocks) * kBlockSize;
+  if (act_dtype == 0)
+    reshape_and_cache_fp8_kernel<F16><<<g, b, 0, stream>>>(kk, vv, kc, vc, slot_mapping, rows, num_kv_heads, slots,
+                                                            k_scale, v_scale);
+  else
+    reshape_and_cache_fp8_kernel<BF16><<<g, b, 0, stream>>>(kk, vv, kc, vc, slot_mapping, rows, num_kv_heads, slots,
+                                                             k_scale, v_scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
-                              int32_t num_kv_heads, int32_t num_blocks, hipStream_t stream) {
+                              int32_t num_kv_heads, int32_t num_blocks, int32_t page_bytes, hipStream_t stream) {
   const int64_t grid = static_cast<int64_t>(num_pairs) * 2 * num_kv_heads;
-  copy_blocks_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(
-      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_pairs, num_kv_heads, num_blocks);
+  copy_blocks_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(page_bytes / 16), 0, stream>>>(
+      static_cast<char*>(k_cache), static_cast<char*>(v_cache), block_pairs, num_kv_heads, num_blocks, page_bytes);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_cache(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                int32_t max_blocks_per_seq, const int32_t* out_offsets, int32_t num_kv_heads,
-                               int32_t num_blocks, hipStream_t stream) {
+                               int32_t num_blocks, bool fp8_cache, hipStream_t stream) {
   const int64_t grid = static_cast<int64_t>(num_seqs) * max_blocks_per_seq;
-  gather_cache_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(
-      static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out), static_cast<const uint16_t*>(k_cache),
-      static_cast<const uint16_t*>(v_cache), block_tables, context_lens, out_offsets, max_blocks_per_seq,
-      num_kv_heads, num_blocks);
+  if (fp8_cache)
+    gather_cache_fp8_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(
+        static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out), static_cast<const uint8_t*>(k_cache),
+        static_cast<const uint8_t*>(v_cache), block_tables, context_lens, out_offsets, max_blocks_per_seq,
+        num_kv_heads, num_blocks);
+  else
+    gather_cache_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(
+        static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out), static_cast<const uint16_t*>(k_cache),
+        static_cast<const uint16_t*>(v_cache), block_tables, context_lens, out_offsets, max_blocks_per_seq,
+        num_kv_heads, num_blocks);
   return hipGetLastError();
 }
 

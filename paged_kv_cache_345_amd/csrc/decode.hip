@@ -139,60 +139,120 @@ __device__ inline void mask_v(uint4 (&vv)[4], int grp, int nvalid) {
   }
 }
 
-// Four contiguous 1 KiB wave loads per K page and per V page, as raw buffer
-// loads: one buffer descriptor per page (wave-uniform, scalar registers, with a
-// 4 KiB record limit) and a single per-lane byte offset shared by K and V.
-// The K loads carry the non-temporal hint and the V loads the default policy.
-// Measured on MI355X over every decode batch: splitting the page traffic
-// evenly between the two policies streams 5-9% faster than either policy
-// alone (all-default or all-non-temporal), and a 3:5 to 6:2 split is as good.
-__device__ inline void load_page(uint4 (&kv)[4], uint4 (&vv)[4], const uint16_t* kp, const uint16_t* vp,
-                                 uint32_t lane_bytes) {
-  const __amdgpu_buffer_rsrc_t kr = page_rsrc(kp);
-  const __amdgpu_buffer_rsrc_t vr = page_rsrc(vp);
-  kv[0] = load16<0, kNonTemporal>(kr, lane_bytes);
-  kv[1] = load16<1024, kNonTemporal>(kr, lane_bytes);
-  kv[2] = load16<2048, kNonTemporal>(kr, lane_bytes);
-  kv[3] = load16<3072, kNonTemporal>(kr, lane_bytes);
-  vv[0] = load16<0>(vr, lane_bytes);
-  vv[1] = load16<1024>(vr, lane_bytes);
-  vv[2] = load16<2048>(vr, lane_bytes);
-  vv[3] = load16<3072>(vr, lane_bytes);
-}
+// Page formats.  Each holds the raw bytes of one block's K page and V page as
+// loaded by a wave, and widens them to the 16-bit fragments the math consumes
+// (kv[i]: lane (grp, col) -> token col, dims 8*(4i + grp) .. +8; vv[p]: tokens
+// 4grp .. 4grp+3 of dims 16*(2p) + col and 16*(2p+1) + col).
+//
+// Each page is read with raw buffer loads: one buffer descriptor per page
+// (wave-uniform, scalar registers, with the page as its record limit) and a
+// single per-lane byte offset shared by K and V.  The K loads carry the
+// non-temporal hint and the V loads the default policy.  Measured on MI355X
+// over every decode batch: splitting the page traffic evenly between the two
+// policies streams 5-9% faster than either policy alone, and a 3:5 to 6:2
+// split is as good.
+
+// 16-bit pages (fp16 / bf16 cache): four contiguous 1 KiB wave loads per page.
+struct Page16 {
+  static constexpr int kPageBytes = 2 * kPageElems;
+  struct Raw {
+    uint4 k[4], v[4];
+  };
+  __device__ static inline void load(Raw& r, const char* kp, const char* vp, uint32_t lane_bytes) {
+    const __amdgpu_buffer_rsrc_t kr = range_rsrc(kp, kPageBytes);
+    const __amdgpu_buffer_rsrc_t vr = range_rsrc(vp, kPageBytes);
+    r.k[0] = load16<0, kNonTemporal>(kr, lane_bytes);
+    r.k[1] = load16<1024, kNonTemporal>(kr, lane_bytes);
+    r.k[2] = load16<2048, kNonTemporal>(kr, lane_bytes);
+    r.k[3] = load16<3072, kNonTemporal>(kr, lane_bytes);
+    r.v[0] = load16<0>(vr, lane_bytes);
+    r.v[1] = load16<1024>(vr, lane_bytes);
+    r.v[2] = load16<2048>(vr, lane_bytes);
+    r.v[3] = load16<3072>(vr, lane_bytes);
+  }
+  __device__ static inline void expand(const Raw& r, uint4 (&kv)[4], uint4 (&vv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kv[i] = r.k[i];
+      vv[i] = r.v[i];
+    }
+  }
+};
+
+// fp8 (E4M3) pages: two contiguous 1 KiB wave loads per page; lane l's 16
+// bytes of load i are its 16-bit fragments 2i and 2i+1, one byte per element,
+// widened exactly to the activation type DT (every E4M3 value is an fp16 and a
+// bf16 value).  The cache scales are applied outside: to the logit scale (K)
+// and to the output (V).
+template <class DT>
+struct PageFp8 {
+  static constexpr int kPageBytes = kPageBytesFp8;
+  struct Raw {
+    uint4 k[2], v[2];
+  };
+  __device__ static inline void load(Raw& r, const char* kp, const char* vp, uint32_t lane_bytes) {
+    const __amdgpu_buffer_rsrc_t kr = range_rsrc(kp, kPageBytes);
+    const __amdgpu_buffer_rsrc_t vr = range_rsrc(vp, kPageBytes);
+    r.k[0] = load16<0, kNonTemporal>(kr, lane_bytes);
+    r.k[1] = load16<1024, kNonTemporal>(kr, lane_bytes);
+    r.v[0] = load16<0>(vr, lane_bytes);
+    r.v[1] = load16<1024>(vr, lane_bytes);
+  }
+  __device__ static inline void widen(uint4 w, uint4& lo, uint4& hi) {
+    lo = make_uint4(DT::template from_e4m3x2<false>(w.x), DT::template from_e4m3x2<true>(w.x),
+                    DT::template from_e4m3x2<false>(w.y), DT::template from_e4m3x2<true>(w.y));
+    hi = make_uint4(DT::template from_e4m3x2<false>(w.z), DT::template from_e4m3x2<true>(w.z),
+                    DT::template from_e4m3x2<false>(w.w), DT::template from_e4m3x2<true>(w.w));
+  }
+  __device__ static inline void expand(const Raw& r, uint4 (&kv)[4], uint4 (&vv)[4]) {
+    widen(r.k[0], kv[0], kv[1]);
+    widen(r.k[1], kv[2], kv[3]);
+    widen(r.v[0], vv[0], vv[1]);
+    widen(r.v[1], vv[2], vv[3]);
+  }
+};
 
 // Streams blocks j0 .. j0 + nb - 1 (nb >= 1) of one sequence's pages of one KV
 // head through `process`, two register sets deep: one block in flight while
 // the other is consumed.  Only the last block takes the masked path.  Block
 // ids are wave-uniform scalar loads (16 per scalar-cache line).
-template <class Process>
+template <class PF, class Process>
 __device__ __attribute__((always_inline)) inline void stream_blocks(const DecodeArgs& a, int s, int kvh, int j0, int nb,
                                                                     int lane, Process&& process) {
   const int32_t* row = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq + j0;
-  const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kPageElems;
-  const int64_t head_off = static_cast<int64_t>(kvh) * kPageElems;
-  auto issue = [&](uint4 (&kv)[4], uint4 (&vv)[4], int jj) __attribute__((always_inline)) {
+  const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * PF::kPageBytes;
+  const int64_t head_off = static_cast<int64_t>(kvh) * PF::kPageBytes;
+  const char* kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache);
+  auto issue = [&](typename PF::Raw& r, int jj) __attribute__((always_inline)) {
     const int bid = row[jj];
     const bool bad = static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks);
     const int64_t off = static_cast<int64_t>(bad ? 0 : bid) * page_stride + head_off;
-    load_page(kv, vv, a.k_cache + off, a.v_cache + off, static_cast<uint32_t>(lane) * 16u);
+    PF::load(r, kc + off, vc + off, static_cast<uint32_t>(lane) * 16u);
   };
-  uint4 ka[4], va[4], kb[4], vb[4];
-  issue(ka, va, 0);
+  // the widened fragments are built when a block is consumed, never held in flight
+  auto consume = [&]<bool kTail>(const typename PF::Raw& r, int j) __attribute__((always_inline)) {
+    uint4 kv[4], vv[4];
+    PF::expand(r, kv, vv);
+    process.template operator()<kTail>(kv, vv, j);
+  };
+  typename PF::Raw ra, rb;
+  issue(ra, 0);
   int jj = 0;
   // steady state: full blocks only and no conditional loads, so each wait
   // leaves the other register set in flight
   for (; jj + 2 < nb; jj += 2) {
-    issue(kb, vb, jj + 1);
-    process.template operator()<false>(ka, va, j0 + jj);
-    issue(ka, va, jj + 2);
-    process.template operator()<false>(kb, vb, j0 + jj + 1);
+    issue(rb, jj + 1);
+    consume.template operator()<false>(ra, j0 + jj);
+    issue(ra, jj + 2);
+    consume.template operator()<false>(rb, j0 + jj + 1);
   }
   if (jj + 1 < nb) {
-    issue(kb, vb, jj + 1);
-    process.template operator()<false>(ka, va, j0 + jj);
-    process.template operator()<true>(kb, vb, j0 + jj + 1);
+    issue(rb, jj + 1);
+    consume.template operator()<false>(ra, j0 + jj);
+    consume.template operator()<true>(rb, j0 + jj + 1);
   } else {
-    process.template operator()<true>(ka, va, j0 + jj);
+    consume.template operator()<true>(ra, j0 + jj);
   }
 }
 
@@ -213,7 +273,7 @@ __device__ inline WaveRange wave_range(const DecodeArgs& a, int nblk, int g, int
 // ---------------------------------------------------------------------------
 // MHA: one query head per KV head.
 // ---------------------------------------------------------------------------
-template <class DT>
+template <class DT, class PF>
 __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(DecodeArgs a) {
   __shared__ float red_o[kWavesPerGroup][kHeadSize];
   __shared__ float red_m[kWavesPerGroup];
@@ -288,7 +348,7 @@ __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(D
         }
       }
     };
-    stream_blocks(a, row_s, h, j_begin, j_count, lane, process);
+    stream_blocks<PF>(a, row_s, h, j_begin, j_count, lane, process);
     z = row_sum16(z);
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = cross_row_sum(acc[j]);
@@ -316,7 +376,7 @@ __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(D
       O = fmaf(c, red_o[w][d], O);
     }
     if (nseg == 1) {
-      out_row[d] = DT::from_f32(O / Z);
+      out_row[d] = DT::from_f32(O / Z * a.out_scale);
     } else {
       const int64_t slot = (static_cast<int64_t>(s) * a.num_heads + h) * a.parts_max + g;
       a.ws_o[slot * kHeadSize + d] = O;
@@ -331,7 +391,7 @@ __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(D
 // ---------------------------------------------------------------------------
 // GQA: up to 16 query heads of one KV head per work-group, on the matrix cores.
 // ---------------------------------------------------------------------------
-template <class DT>
+template <class DT, class PF>
 __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   __shared__ float red_o[kWavesPerGroup][16][kHeadSize];
   __shared__ float red_m[kWavesPerGroup][16];
@@ -422,7 +482,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
         O[jd] = DT::mfma_pv(pa, b, O[jd]);
       }
     };
-    stream_blocks(a, s, kvh, wr.j0, wr.nb, lane, process);
+    stream_blocks<PF>(a, s, kvh, wr.j0, wr.nb, lane, process);
   }
 
   // this wave's state: O[j][r] is head 4grp + r, dim 16j + col; m and the
@@ -462,10 +522,11 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     if (wr.nseg == 1) {
       uint16_t* orow = out_seq + static_cast<int64_t>(h0 + hh) * kHeadSize + d0;
       uint4 packed;
-      packed.x = DT::pack2(o[0] / Z, o[1] / Z);
-      packed.y = DT::pack2(o[2] / Z, o[3] / Z);
-      packed.z = DT::pack2(o[4] / Z, o[5] / Z);
-      packed.w = DT::pack2(o[6] / Z, o[7] / Z);
+      const float os = a.out_scale;
+      packed.x = DT::pack2(o[0] / Z * os, o[1] / Z * os);
+      packed.y = DT::pack2(o[2] / Z * os, o[3] / Z * os);
+      packed.z = DT::pack2(o[4] / Z * os, o[5] / Z * os);
+      packed.w = DT::pack2(o[6] / Z * os, o[7] / Z * os);
       *reinterpret_cast<uint4*>(orow) = packed;
     } else {
       const int64_t slot = (static_cast<int64_t>(s) * a.num_heads + h0 + hh) * a.parts_max + g;
@@ -481,8 +542,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of segment partials: one work-group per (seq, head).
-//   M = max_p m_p,  c_p = 2^(m_p - M),  out = sum_p c_p O_p / sum_p c_p Z_p
+// Log-sum-exp merge of segment partials.
 // ---------------------------------------------------------------------------
 // One wave per (sequence, head) row with more than one segment; 4 rows per
 // work-group:
@@ -519,7 +579,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
       o0 = fmaf(c, v.x, o0);
       o1 = fmaf(c, v.y, o1);
     }
-    reinterpret_cast<uint32_t*>(a.out + row * kHeadSize)[lane] = DT::pack2(o0 / z, o1 / z);
+    reinterpret_cast<uint32_t*>(a.out + row * kHeadSize)[lane] = DT::pack2(o0 / z * a.out_scale, o1 / z * a.out_scale);
     return;
   }
 
@@ -550,22 +610,23 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   for (int i = 0; i < 8; ++i) acc[i] = cross_row_sum(acc[i]);
   if (sg == 0) {
     uint4 packed;
-    packed.x = DT::pack2(acc[0] / z, acc[1] / z);
-    packed.y = DT::pack2(acc[2] / z, acc[3] / z);
-    packed.z = DT::pack2(acc[4] / z, acc[5] / z);
-    packed.w = DT::pack2(acc[6] / z, acc[7] / z);
+    const float os = a.out_scale;
+    packed.x = DT::pack2(acc[0] / z * os, acc[1] / z * os);
+    packed.y = DT::pack2(acc[2] / z * os, acc[3] / z * os);
+    packed.z = DT::pack2(acc[4] / z * os, acc[5] / z * os);
+    packed.w = DT::pack2(acc[6] / z * os, acc[7] / z * os);
     reinterpret_cast<uint4*>(a.out + row * kHeadSize)[dg] = packed;
   }
 }
 
-template <class DT>
+template <class DT, class PF>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const int64_t grid = item_grid(a);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (a.group == 1)
-    decode_mha_kernel<DT><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
+    decode_mha_kernel<DT, PF><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
   else
-    decode_gqa_kernel<DT><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
+    decode_gqa_kernel<DT, PF><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.parts_max > 1) {
@@ -576,8 +637,10 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   return err;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream) {
-  return dtype == 0 ? launch_decode_t<F16>(a, stream) : launch_decode_t<BF16>(a, stream);
+hipError_t launch_decode(const DecodeArgs& a, int act_dtype, bool fp8_cache, hipStream_t stream) {
+  if (fp8_cache)
+    return act_dtype == 0 ? launch_decode_t<F16, PageFp8<F16>>(a, stream) : launch_decode_t<BF16, PageFp8<BF16>>(a, stream);
+  return act_dtype == 0 ? launch_decode_t<F16, Page16>(a, stream) : launch_decode_t<BF16, Page16>(a, stream);
 }
 
 }  // namespace pkv

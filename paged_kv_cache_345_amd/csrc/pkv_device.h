@@ -39,6 +39,21 @@ __host__ __device__ inline int v_page_offset(int t, int d) {
   return (j >> 1) * 512 + (16 * grp + c) * 8 + (j & 1) * 4 + i;
 }
 
+// fp8 (E4M3) pages: 16 tokens x 128 dims of one byte, 2 KiB.  A wave reads a
+// page as two contiguous 1 KiB loads of 16 bytes per lane, and lane l's 16
+// bytes of load i, widened to 16-bit values, are exactly its two 16-byte
+// fragments 2i and 2i+1 of the 16-bit layout above (byte order = element
+// order), so the same matrix-core and dot-product code consumes them:
+//   K: byte (d/64)*1024 + (16*((d/8)%4) + t)*16 + ((d/32)%2)*8 + d%8
+//   V: byte (d/64)*1024 + (16*(t/4) + d%16)*16 + ((d/32)%2)*8 + ((d/16)%2)*4 + t%4
+constexpr int kPageBytesFp8 = kPageElems;  // 2048
+__host__ __device__ inline int k_page_offset_fp8(int t, int d) {
+  return (d >> 6) * 1024 + (16 * ((d >> 3) & 3) + t) * 16 + ((d >> 5) & 1) * 8 + (d & 7);
+}
+__host__ __device__ inline int v_page_offset_fp8(int t, int d) {
+  return (d >> 6) * 1024 + (16 * (t >> 2) + (d & 15)) * 16 + ((d >> 5) & 1) * 8 + ((d >> 4) & 1) * 4 + (t & 3);
+}
+
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -52,6 +67,11 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 struct F16 {
   static constexpr int kMhaWavesPerSimd = 5;  // MHA decode fits 5 waves per SIMD (<= 102 VGPRs)
+  // two E4M3 codes (bytes 2*hi, 2*hi+1 of w) -> two fp16 values, exact
+  template <bool kHi>
+  __device__ static inline uint32_t from_e4m3x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi));
+  }
   __device__ static inline float lo(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[0]; }
   __device__ static inline float hi(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[1]; }
   __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
@@ -75,6 +95,10 @@ struct F16 {
 
 struct BF16 {
   static constexpr int kMhaWavesPerSimd = 4;  // the bf16 widening needs more registers
+  template <bool kHi>
+  __device__ static inline uint32_t from_e4m3x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+  }
   __device__ static inline float lo(uint32_t w) { return __uint_as_float(w << 16); }
   __device__ static inline float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
   __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
@@ -163,6 +187,7 @@ __device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* page) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(page), 0, kPageElems * 2, kBufferDword3);
 }
 typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef int int2_t __attribute__((ext_vector_type(2)));
 // Cache-policy operand of the gfx950 buffer loads: 0 is the default policy,
 // kNonTemporal sets the instruction's nt bit (streaming data, not expected to
 // be reused).
@@ -176,6 +201,11 @@ __device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t lane_off) {
                             __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(lane_off), kConstOff, kPolicy));
 }
 
+// Buffer descriptor covering n bytes starting at p.
+__device__ inline __amdgpu_buffer_rsrc_t range_rsrc(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, kBufferDword3);
+}
+
 // Stores through a page descriptor, at a byte offset inside the page.
 template <int kPolicy = kDefaultPolicy>
 __device__ inline void store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint4 x) {
@@ -184,6 +214,40 @@ __device__ inline void store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint
 template <int kPolicy = kDefaultPolicy>
 __device__ inline void store2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint16_t x) {
   __builtin_amdgcn_raw_buffer_store_b16(x, r, static_cast<int>(byte_off), 0, kPolicy);
+}
+
+template <int kPolicy = kDefaultPolicy>
+__device__ inline void store8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint2 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2_t, x), r, static_cast<int>(byte_off), 0, kPolicy);
+}
+template <int kPolicy = kDefaultPolicy>
+__device__ inline void store1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint8_t x) {
+  __builtin_amdgcn_raw_buffer_store_b8(x, r, static_cast<int>(byte_off), 0, kPolicy);
+}
+
+// E4M3 code of a float (OCP 8-bit floating point: 1 sign, 4 exponent bits with
+// bias 7, 3 mantissa bits, subnormals m/8 * 2^-6, no infinities, S.1111.111 =
+// NaN, largest finite 448): the nearest value, ties to the even mantissa;
+// magnitudes of 448 and beyond (infinity included) give +-448, NaN gives a NaN
+// code, and the sign of zero is kept.  Written from the format's definition:
+// the subnormal range is a grid of step 2^-9 (rounded with the float unit's
+// round-to-nearest-even), the normal range keeps 3 of the 23 mantissa bits.
+__device__ inline uint32_t e4m3_encode(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t au = u & 0x7FFFFFFFu;
+  if (au > 0x7F800000u) return sign | 0x7Fu;  // NaN
+  if (au >= 0x43E00000u) return sign | 0x7Eu;  // |x| >= 448
+  if (au < 0x3C800000u) {                      // |x| < 2^-6: multiples of 2^-9
+    // exact scaling; values below 2^-126 read as zero here and round to 0 anyway
+    const float grid = __uint_as_float(au) * 512.0f;
+    return sign | static_cast<uint32_t>(__builtin_rintf(grid));  // 8 is the code of 2^-6
+  }
+  const uint32_t mant = au & 0x7FFFFFu;
+  uint32_t q = (((au >> 23) - 120u) << 3) | (mant >> 20);  // exponent bias 127 -> 7
+  const uint32_t rem = mant & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;  // a mantissa carry bumps the exponent
+  return sign | (q > 0x7Eu ? 0x7Eu : q);
 }
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -34,7 +34,8 @@ struct DecodeArgs {
   float* ws_o;     // [S, Hq, parts_max, 128] unnormalised partial outputs
   float* ws_ml;    // [S, Hq, parts_max, 2]   (running max in log2 units, Z)
   int* plan;       // work-list plan (planned mode) or null
-  float scale_log2e;
+  float scale_log2e;  // logit scale (times the K scale of an fp8 cache) in log2 units
+  float out_scale;    // 1, or the V scale of an fp8 cache
   int num_seqs;
   int num_heads;
   int num_kv_heads;
@@ -59,16 +60,21 @@ struct PlanArgs {
   int parts_max;
 };
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
+// act_dtype: 0 fp16, 1 bf16 (q, out); fp8_cache: the pages hold E4M3 codes
+hipError_t launch_decode(const DecodeArgs& a, int act_dtype, bool fp8_cache, hipStream_t stream);
 hipError_t launch_decode_plan(const PlanArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                                     int32_t num_blocks, hipStream_t stream);
+hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                                        const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t num_blocks, int act_dtype, float k_scale, float v_scale,
+                                        hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
-                              int32_t num_kv_heads, int32_t num_blocks, hipStream_t stream);
+                              int32_t num_kv_heads, int32_t num_blocks, int32_t page_bytes, hipStream_t stream);
 hipError_t launch_gather_cache(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                int32_t max_blocks_per_seq, const int32_t* out_offsets, int32_t num_kv_heads,
-                               int32_t num_blocks, hipStream_t stream);
+                               int32_t num_blocks, bool fp8_cache, hipStream_t stream);
 
 }  // namespace pkv

@@ -188,3 +188,81 @@ def test_library_binds_to_torch_hip_runtime():
             "print(len([x for x in libs if 'amdhip64' in x]), len([x for x in libs if 'hsa-runtime64' in x]))")
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, check=True)
     assert out.stdout.split() == ["1", "1"], out.stdout
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) cache
+# ---------------------------------------------------------------------------
+
+def _k8(t, d):
+    return (d // 64) * 1024 + (16 * ((d // 8) % 4) + t) * 16 + ((d // 32) % 2) * 8 + d % 8
+
+
+def _v8(t, d):
+    return (d // 64) * 1024 + (16 * (t // 4) + d % 16) * 16 + ((d // 32) % 2) * 8 + ((d // 16) % 2) * 4 + t % 4
+
+
+def test_fp8_page_layout_matches_documented_formula():
+    desc = pkv.CacheDesc(5, 16, 3, 128, pkv.PKV_FP8_E4M3)
+    for b, h in ((0, 0), (4, 2)):
+        base = (b * 3 + h) * 2048
+        ks = {pkv.k_index(desc, b, h, t, d) for t in range(16) for d in range(128)}
+        vs = {pkv.v_index(desc, b, h, t, d) for t in range(16) for d in range(128)}
+        assert ks == set(range(base, base + 2048)) == vs
+        for t, d in ((0, 0), (15, 127), (7, 77), (3, 64)):
+            assert pkv.k_index(desc, b, h, t, d) == base + _k8(t, d)
+            assert pkv.v_index(desc, b, h, t, d) == base + _v8(t, d)
+
+
+def test_fp8_lane_bytes_are_the_16bit_fragments():
+    """Byte b of lane l in fp8 load i (page bytes 1024 i + 16 l + b) holds the
+    element that the 16-bit layout gives lane l as element b % 8 of its
+    fragment 2i + b / 8, so widening reproduces the 16-bit operands."""
+    for i in range(2):
+        for lane in range(64):
+            for b in range(16):
+                j, e = 2 * i + b // 8, b % 8
+                off = 1024 * i + 16 * lane + b
+                t, d = lane % 16, 8 * (4 * j + lane // 16) + e
+                assert _k8(t, d) == off and _k_formula(t, d) == 512 * j + 8 * lane + e
+                t, d = 4 * (lane // 16) + e % 4, 16 * (2 * j + e // 4) + lane % 16
+                assert _v8(t, d) == off and _v_formula(t, d) == 512 * j + 8 * lane + e
+
+
+def test_fp8_cache_bytes_and_workspace():
+    d8 = pkv.CacheDesc(64, 16, 8, 128, pkv.PKV_FP8_E4M3)
+    assert pkv.lib().pkv_cache_bytes(ctypes.byref(d8)) == 64 * 8 * 2048
+    assert pkv.workspace_size(128, 64, 511, d8) > 0
+    assert pkv.partition_tokens_for(128, 8, 128, d8) % 16 == 0
+
+
+def _scales(act=pkv.PKV_F16, ks=0.02, vs=0.03):
+    return ctypes.byref(pkv.Fp8Scales(act, ks, vs))
+
+
+def test_fp8_argument_errors_return_before_launch():
+    """Every case here fails its argument checks, so nothing is launched (the
+    device pointers are placeholders)."""
+    L = pkv.lib()
+    p = 1 << 20
+    d8 = pkv.CacheDesc(64, 16, 8, 128, pkv.PKV_FP8_E4M3)
+    d16 = pkv.CacheDesc(64, 16, 8, 128, pkv.PKV_F16)
+
+    def dec(desc, sc, fn=L.paged_attn_decode_fp8, scale=1.0):
+        return fn(p, p, p, p, p, p, scale, 8, 4, 8, 10, ctypes.byref(desc), sc, 0, p, 1 << 30, None)
+
+    # the 16-bit entry points refuse an fp8 cache; the fp8 ones a 16-bit cache
+    assert _decode_status(d8, ws=p, ws_bytes=1 << 30) == pkv.PKV_ERR_UNSUPPORTED
+    assert dec(d16, _scales()) == pkv.PKV_ERR_INVALID
+    assert dec(d16, _scales(), fn=L.paged_attn_decode_run_fp8) == pkv.PKV_ERR_INVALID
+    assert dec(d8, None) == pkv.PKV_ERR_INVALID
+    for ks, vs in ((0.0, 1.0), (-1.0, 1.0), (float("nan"), 1.0), (1.0, float("inf"))):
+        assert dec(d8, _scales(ks=ks, vs=vs)) == pkv.PKV_ERR_INVALID
+    assert dec(d8, _scales(act=pkv.PKV_FP8_E4M3)) == pkv.PKV_ERR_UNSUPPORTED
+    assert dec(d8, _scales(), scale=float("nan")) == pkv.PKV_ERR_INVALID
+    assert L.reshape_and_cache(p, p, p, p, p, 4, ctypes.byref(d8), None) == pkv.PKV_ERR_UNSUPPORTED
+    assert L.reshape_and_cache_fp8(p, p, p, p, p, 4, ctypes.byref(d16), _scales(), None) == pkv.PKV_ERR_INVALID
+    assert L.reshape_and_cache_fp8(p, p, p, p, p, 4, ctypes.byref(d8), None, None) == pkv.PKV_ERR_INVALID
+    assert L.reshape_and_cache_fp8(p, p, p, p, p, 4, ctypes.byref(d8), _scales(ks=0.0), None) == pkv.PKV_ERR_INVALID
+    assert L.reshape_and_cache_fp8(p, p, p, p, p, -1, ctypes.byref(d8), _scales(), None) == pkv.PKV_ERR_INVALID
+    assert L.reshape_and_cache_fp8(None, None, None, None, None, 0, ctypes.byref(d8), _scales(), None) == pkv.PKV_OK
