@@ -39,17 +39,20 @@ def log(msg: str) -> None:
 
 def step_bytes(wl, step):
     """Algorithmic bytes of one step.  K/V: every unique live (block, slot) once,
-    2 * Hkv * 128 * 2 bytes each (parallel samples that share a prompt block
-    count it once); plus q and out, one 4-byte block-table entry per logical
-    block and one context length per sequence; plus the copy-on-write pages
-    (read + write) and the new tokens' rows (read + write) and slots."""
+    2 * Hkv * 128 * cb bytes each, cb = 2 (fp16/bf16 cache) or 1 (fp8 cache)
+    (parallel samples that share a prompt block count it once); plus q and out
+    (2 bytes per element), one 4-byte block-table entry per logical block and
+    one context length per sequence; plus the copy-on-write pages (read +
+    write) and the new tokens' rows (2-byte rows read, cache elements written)
+    and slots."""
     import numpy as np
 
-    eb = 2
+    eb = 2  # q, out and the new rows
+    cb = 1 if wl.kv_dtype == "fp8e4m3" else 2  # one cache element
     hkv, hq, D = wl.num_kv_heads, wl.num_heads, 128
     S = wl.num_seqs
     lens = wl.context_lens.astype(np.int64)
-    per_token = 2 * hkv * D * eb  # K and V rows of one token, all KV heads
+    per_token = 2 * hkv * D * cb  # K and V rows of one token, all KV heads
     tables = step.block_tables_host
     live = set()
     for s in range(S):
@@ -65,9 +68,9 @@ def step_bytes(wl, step):
     meta = nblk * 4 + S * 4
     decode = kv_unique + qo + meta
     n_pairs = int(step.block_pairs_host.shape[0])
-    copy = n_pairs * 2 * hkv * 2048 * eb * 2  # K and V pages of every head, read + write
+    copy = n_pairs * 2 * hkv * 2048 * cb * 2  # K and V pages of every head, read + write
     T = int(step.slot_mapping_host.shape[0])
-    write = T * hkv * D * eb * 2 * 2 + T * 4  # K and V rows read + written, slots read
+    write = T * hkv * D * 2 * (eb + cb) + T * 4  # K and V rows read, cache elements written, slots read
     return dict(kv_per_sequence=kv_seq, kv_unique=kv_unique, decode=decode, copy=copy, write=write,
                 step=decode + copy + write, q_out=qo, meta=meta)
 
@@ -117,8 +120,13 @@ def cpu_baseline(wl, seconds: float):
     while wall < seconds:
         for s in range(wl.num_seqs):
             t0, c0 = time.perf_counter(), time.process_time()
-            oracle.paged_decode_ref(wl.q, ref.k_cache, ref.v_cache, ref.block_tables, ref.context_lens,
-                                    wl.scale, wl.num_kv_heads, wl.dtype, seqs=[s])
+            if wl.kv_dtype == "fp8e4m3":
+                oracle.fp8.paged_decode_fp8_ref(wl.q, ref.k_cache, ref.v_cache, ref.block_tables, ref.context_lens,
+                                                wl.scale, wl.num_kv_heads, wl.dtype, wl.k_scale, wl.v_scale,
+                                                seqs=[s])
+            else:
+                oracle.paged_decode_ref(wl.q, ref.k_cache, ref.v_cache, ref.block_tables, ref.context_lens,
+                                        wl.scale, wl.num_kv_heads, wl.dtype, seqs=[s])
             wall += time.perf_counter() - t0
             cpu += time.process_time() - c0
             nbytes += int(wl.context_lens[s]) * per_token
@@ -131,7 +139,7 @@ def cpu_baseline(wl, seconds: float):
         "unit": "GB/s",
         "cores": max(1, int(round(cpu / wall))),
         "kind": "oracle",
-        "sample": (f"fp64 numpy paged decode (oracle.paged_decode_ref), {seqs_done} sequence evaluations "
+        "sample": (f"fp64 numpy paged decode (oracle paged decode reference), {seqs_done} sequence evaluations "
                    f"= {seqs_done / wl.num_seqs:.2f} passes over the {wl.num_seqs}-sequence batch, all "
                    f"{wl.num_heads} heads, {wall:.1f} s wall; per-sequence KV bytes / wall time"),
         "host_cpus": len(os.sched_getaffinity(0)),
@@ -245,7 +253,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": wl.dtype if wl.kv_dtype == wl.dtype else f"{wl.dtype} (fp8e4m3 cache)",
         "data": "synthetic",
         "config": {
             "workload": wl.spec.description,
@@ -259,7 +267,10 @@ def main() -> int:
             "partition_tokens": pkv.partition_tokens_for(S, wl.num_heads, step.max_blocks, step.desc,
                                                          step.partition_tokens),
             "copy_pairs": int(step.block_pairs_host.shape[0]),
-            "step": "copy_blocks + reshape_and_cache + paged_attn_decode_plan + paged_attn_decode_run",
+            "kv_cache_dtype": wl.kv_dtype,
+            "step": ("copy_blocks + reshape_and_cache + paged_attn_decode_plan + paged_attn_decode_run"
+                     if wl.kv_dtype == wl.dtype else
+                     "copy_blocks + reshape_and_cache_fp8 + paged_attn_decode_plan + paged_attn_decode_run_fp8"),
             "parallelism": "single GPU",
         },
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
