@@ -25,6 +25,8 @@ What it computes, in float64 from the same fp16/bf16 values the GPU reads:
   per-sequence K/V, independent of everything above.
 * ``partition_partials_ref`` / ``lse_merge_ref`` — the same softmax split into
   token partitions and recombined by the log-sum-exp identity.
+* ``prefill_ref`` — multi-token-query (chunked prefill) attention over the
+  paged cache, causal by absolute position (readings in ``oracle/prefill.py``).
 * ``fp8`` — the fp8 (E4M3) KV cache variant: the E4M3 codec written from its
   definition, the quantising slot-mapped write and decode attention over the
   dequantised rows (readings stated in ``oracle/fp8.py``).
@@ -46,6 +48,7 @@ from .attention import (
 )
 from .runner import OracleStep, run_decode_step
 from . import fp8
+from .prefill import prefill_ref
 
 __all__ = [
     "to_f64",
@@ -62,4 +65,5 @@ __all__ = [
     "OracleStep",
     "run_decode_step",
     "fp8",
+    "prefill_ref",
 ]

@@ -52,6 +52,10 @@ __all__ = [
     "round_bf16_bits",
     "storage_dtype",
     "thread_map",
+    "PrefillWorkload",
+    "make_prefill_workload",
+    "PREFILL_CONFIGS",
+    "make_prefill",
 ]
 
 
@@ -394,3 +398,94 @@ def make_random_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_hea
     q = _to_storage(rng.standard_normal((num_seqs, num_heads, HEAD_SIZE), dtype=np.float32), dtype)
     return Workload(spec=spec, context_lens=lens, free_order=free_order, q=q,
                     key_scales=key_scales, groups=grp, ops=_ops_for(lens, grp))
+
+
+# --------------------------------------------------------------------------
+# chunked prefill (multi-token queries over the paged cache)
+# --------------------------------------------------------------------------
+
+@dataclass
+class PrefillWorkload:
+    """Sequence s holds ``context_lens[s]`` tokens in the cache (all written by
+    the slot-mapped write); its last ``chunk_lens[s]`` tokens are the chunk whose
+    queries attend causally to the cache.  ``q`` is ``[sum(chunk_lens), Hq, D]``,
+    sequence-major.  Streams: main ``default_rng(seed)`` (lengths, chunk lengths,
+    pool permutation, q), per-sequence ``default_rng([seed, 3, s])`` (K then V
+    rows of all its tokens)."""
+
+    name: str
+    seed: int
+    num_heads: int
+    num_kv_heads: int
+    dtype: str
+    context_lens: np.ndarray  # int64 [S]
+    chunk_lens: np.ndarray  # int64 [S]
+    free_order: np.ndarray  # int32 [pool]
+    q: np.ndarray  # storage dtype [Tq, Hq, D]
+    key_scales: Optional[np.ndarray] = None
+    description: str = ""
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def pool_blocks(self) -> int:
+        return int(self.free_order.shape[0])
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(HEAD_SIZE)
+
+    @property
+    def query_start(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.chunk_lens)]).astype(np.int64)
+
+    @property
+    def num_query_tokens(self) -> int:
+        return int(self.chunk_lens.sum())
+
+    def seq_kv(self, s: int):
+        """K, V rows of all context_lens[s] tokens of sequence s: [L_s, Hkv, D]."""
+        rng = np.random.default_rng([self.seed, 3, s])
+        n, hkv = int(self.context_lens[s]), self.num_kv_heads
+        k = rng.standard_normal((n, hkv, HEAD_SIZE), dtype=np.float32)
+        if self.key_scales is not None:
+            k *= self.key_scales[None, :, None]
+        v = rng.standard_normal((n, hkv, HEAD_SIZE), dtype=np.float32)
+        return _to_storage(k, self.dtype), _to_storage(v, self.dtype)
+
+
+def make_prefill_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_heads: int, dtype: str,
+                          context: Tuple[int, int], chunk: Tuple[int, int], key_scale=None, pool_slack: int = 4,
+                          name: str = "", description: str = "") -> PrefillWorkload:
+    """Contexts U[context], chunk lengths U[chunk] clipped to the context."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(context[0], context[1], num_seqs, endpoint=True).astype(np.int64)
+    chunks = np.minimum(rng.integers(chunk[0], chunk[1], num_seqs, endpoint=True), lens).astype(np.int64)
+    pool = int(sum(-(-int(L) // BLOCK_SIZE) for L in lens)) + pool_slack
+    free_order = rng.permutation(pool).astype(np.int32)
+    key_scales = None
+    if key_scale is not None:
+        key_scales = rng.uniform(key_scale[0], key_scale[1], num_kv_heads).astype(np.float32)
+    q = _to_storage(rng.standard_normal((int(chunks.sum()), num_heads, HEAD_SIZE), dtype=np.float32), dtype)
+    return PrefillWorkload(name=name or f"prefill{seed}", seed=seed, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                           dtype=dtype, context_lens=lens, chunk_lens=chunks, free_order=free_order, q=q,
+                           key_scales=key_scales, description=description)
+
+
+PREFILL_CONFIGS = {
+    "prefill_llama13b": dict(seed=21, num_seqs=16, num_heads=40, num_kv_heads=40, dtype="fp16",
+                             context=(1024, 4096), chunk=(512, 512),
+                             description="chunked prefill, LLaMA-13B-shaped: 16 seqs, 40 MHA heads, fp16, "
+                                         "contexts U[1024,4096], the last 512 tokens of each as the chunk"),
+    "prefill_gqa": dict(seed=22, num_seqs=16, num_heads=64, num_kv_heads=8, dtype="bf16",
+                        context=(1024, 8192), chunk=(512, 512), key_scale=(0.5, 2.0),
+                        description="chunked prefill, GQA: 16 seqs, 64 query / 8 KV heads, bf16, "
+                                    "contexts U[1024,8192], the last 512 tokens of each as the chunk"),
+}
+
+
+def make_prefill(name: str) -> PrefillWorkload:
+    cfg = dict(PREFILL_CONFIGS[name])
+    return make_prefill_workload(cfg.pop("seed"), name=name, **cfg)
