@@ -224,3 +224,103 @@ def build_step(wl: synth.Workload, device="cuda", *, garbage: str = "nan", garba
     if run:
         step.run_step()
     return step
+
+
+@dataclass
+class GpuPrefill:
+    """A chunked-prefill call on the GPU: the caches hold every token of every
+    sequence; ``run`` evaluates the chunks' queries."""
+    wl: object  # synth.PrefillWorkload
+    k_cache: object
+    v_cache: object
+    q: object
+    out: object
+    block_tables: object
+    context_lens: object
+    query_start: object
+    workspace: Optional[object]
+    partition_tokens: int
+    max_blocks: int
+    block_tables_host: np.ndarray
+
+    @property
+    def fp8(self) -> bool:
+        return self.wl.kv_dtype == "fp8e4m3"
+
+    def run(self, out=None, stream=None, block_tables=None, k_cache=None, v_cache=None):
+        out = self.out if out is None else out
+        kw = dict(k_scale=self.wl.k_scale, v_scale=self.wl.v_scale) if self.fp8 else {}
+        pkv.paged_attn_prefill(out, self.q, self.k_cache if k_cache is None else k_cache,
+                               self.v_cache if v_cache is None else v_cache,
+                               self.block_tables if block_tables is None else block_tables, self.context_lens,
+                               self.query_start, self.wl.scale, self.wl.num_kv_heads,
+                               max_query_len=int(self.wl.chunk_lens.max()), partition_tokens=self.partition_tokens,
+                               workspace=self.workspace, stream=stream, **kw)
+        return out
+
+
+def build_prefill(wl, device="cuda", *, garbage: str = "nan", garbage_seed: int = 0,
+                  partition_tokens: int = 0, run: bool = True, fill_chunk_tokens: int = 1 << 16) -> GpuPrefill:
+    """Place every token of every sequence with the library's block manager,
+    write their rows with reshape_and_cache[_fp8] and (if ``run``) evaluate the
+    chunks with paged_attn_prefill."""
+    import torch
+
+    dtype = wl.dtype
+    tdt = torch_dtype(dtype)
+    fp8 = wl.kv_dtype == "fp8e4m3"
+    cdt = torch.uint8 if fp8 else tdt
+    k_cache, v_cache = pkv.allocate_cache(wl.pool_blocks, wl.num_kv_heads, cdt, device)
+    bits = torch.uint8 if fp8 else torch.int16
+    if garbage == "nan":
+        k_cache.view(bits).fill_(255 if fp8 else -1)
+        v_cache.view(bits).fill_(255 if fp8 else -1)
+    elif garbage == "random":
+        g = torch.Generator(device=device)
+        g.manual_seed(garbage_seed)
+        lo, hi = (0, 256) if fp8 else (-32768, 32767)
+        for c in (k_cache, v_cache):
+            c.view(bits).copy_(torch.randint(lo, hi, c.shape, generator=g, device=device, dtype=bits))
+    elif garbage != "none":
+        raise ValueError(garbage)
+    bm = pkv.BlockManager(wl.pool_blocks, BS, wl.free_order)
+    pending, n_pending = [], 0
+
+    def flush():
+        nonlocal n_pending
+        if not pending:
+            return
+        slots = np.concatenate([c[0] for c in pending]).astype(np.int32)
+        k = np.concatenate([c[1] for c in pending])
+        v = np.concatenate([c[2] for c in pending])
+        write_rows(wl, to_device(k, dtype, device), to_device(v, dtype, device), k_cache, v_cache,
+                   torch.from_numpy(slots).to(device))
+        pending.clear()
+        n_pending = 0
+
+    for s in range(wl.num_seqs):
+        slots = bm.add(s, int(wl.context_lens[s]))
+        k, v = wl.seq_kv(s)
+        pending.append((slots, k, v))
+        n_pending += slots.shape[0]
+        if n_pending >= fill_chunk_tokens:
+            flush()
+    flush()
+    S = wl.num_seqs
+    max_blocks = max(bm.num_seq_blocks(s) for s in range(S))
+    tables = bm.block_table(range(S), max_blocks)
+    desc = pkv.cache_desc(wl.pool_blocks, wl.num_kv_heads, cdt)
+    tq = wl.num_query_tokens
+    ws_bytes = pkv.prefill_workspace_size(S, wl.num_heads, max_blocks, tq, int(wl.chunk_lens.max()), desc,
+                                          partition_tokens)
+    pre = GpuPrefill(
+        wl=wl, k_cache=k_cache, v_cache=v_cache, q=to_device(wl.q, dtype, device),
+        out=torch.empty((tq, wl.num_heads, 128), dtype=tdt, device=device),
+        block_tables=torch.from_numpy(tables).to(device),
+        context_lens=torch.from_numpy(wl.context_lens.astype(np.int32)).to(device),
+        query_start=torch.from_numpy(wl.query_start.astype(np.int32)).to(device),
+        workspace=torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None,
+        partition_tokens=partition_tokens, max_blocks=max_blocks, block_tables_host=tables)
+    if run:
+        pre.run()
+    return pre

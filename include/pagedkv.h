@@ -258,6 +258,52 @@ pkv_status paged_attn_decode_run_fp8(void* out, const void* q, const void* k_cac
                                      int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/* ---------------------------------------------------------------------------
+ * paged_attn_prefill — multi-token-query attention over the paged cache, for
+ * chunked prefill ([repo] §2.2: the prefill of a long prompt is cut into
+ * chunks that run alongside decode; the causal reading below is this
+ * library's).  Sequence s has context_lens[s] tokens in the cache, the last
+ * C_s = query_start[s+1] - query_start[s] of which are its chunk (already
+ * written by reshape_and_cache).  Chunk query j sits at position
+ * p = context_lens[s] - C_s + j and attends to cache tokens 0..p:
+ *
+ *   out[query_start[s] + j, h, :] =
+ *       sum_{t <= p} softmax_t(scale * q[query_start[s]+j, h, :] . K[s,t,kvh,:]) V[s,t,kvh,:]
+ *
+ *   q, out           [num_query_tokens, num_heads, 128], cache dtype (16-bit
+ *                    caches) or act_dtype (fp8 form)
+ *   query_start      int32 [num_seqs + 1], non-decreasing, query_start[0] = 0,
+ *                    query_start[num_seqs] = num_query_tokens, C_s <= context_lens[s]
+ *   max_query_len    >= every C_s (sizes the grid; queries of a longer chunk
+ *                    past max_query_len are not written)
+ *   other arguments  as paged_attn_decode; the workspace holds fp32 segment
+ *                    partials per (query token, head) when a work-group's key
+ *                    range spans several segments; its size is
+ *                    paged_attn_prefill_workspace_size().
+ * One work-group takes 64 (query position, head) rows of one KV head (16 per
+ * wave) and streams the keys up to its last position on the matrix cores;
+ * keys beyond a row's position are masked.  Tolerance and errors as decode.
+ * ------------------------------------------------------------------------- */
+size_t paged_attn_prefill_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                         int32_t num_query_tokens, int32_t max_query_len,
+                                         int32_t partition_tokens, const pkv_cache_desc* cache);
+pkv_status paged_attn_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              const int32_t* query_start, float scale, int32_t num_kv_heads,
+                              int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                              int32_t num_query_tokens, int32_t max_query_len,
+                              const pkv_cache_desc* cache, int32_t partition_tokens,
+                              void* workspace, size_t workspace_bytes, void* stream);
+/* The same over an fp8 cache (see the fp8 section above). */
+pkv_status paged_attn_prefill_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* query_start, float scale, int32_t num_kv_heads,
+                                  int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                  int32_t num_query_tokens, int32_t max_query_len,
+                                  const pkv_cache_desc* cache, const pkv_fp8_scales* scales,
+                                  int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 const char* pkv_status_string(pkv_status s);
 const char* pkv_version(void);
 

@@ -74,6 +74,11 @@ SIGNATURES = {
     "paged_attn_decode_run": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _i32,
                                      _vp, _sz, _vp]),
     "paged_attn_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _DP]),
+    "paged_attn_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _DP]),
+    "paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _i32, _i32, _DP,
+                                  _i32, _vp, _sz, _vp]),
+    "paged_attn_prefill_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _DP, _SP, _i32, _vp, _sz, _vp]),
     "paged_attn_decode_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _DP]),
     "reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _DP, _vp]),
     "reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _DP, _SP, _vp]),
@@ -345,6 +350,58 @@ def paged_attn_decode_run_fp8(out, q, k_cache, v_cache, block_tables, context_le
     return out
 
 
+def prefill_workspace_size(num_seqs: int, num_heads: int, max_blocks_per_seq: int, num_query_tokens: int,
+                           max_query_len: int, desc: CacheDesc, partition_tokens: int = 0) -> int:
+    n = lib().paged_attn_prefill_workspace_size(num_seqs, num_heads, max_blocks_per_seq, num_query_tokens,
+                                                max_query_len, partition_tokens, ctypes.byref(desc))
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedKVError(PKV_ERR_INVALID, "paged_attn_prefill_workspace_size")
+    return int(n)
+
+
+def paged_attn_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
+                       num_kv_heads: int, *, max_query_len: int, k_scale: Optional[float] = None,
+                       v_scale: Optional[float] = None, partition_tokens: int = 0, workspace=None, stream=None):
+    """Chunked-prefill attention: chunk query j of sequence s (row
+    query_start[s] + j) attends to cache tokens 0 .. context_lens[s] - C_s + j.
+    With k_scale / v_scale the cache is fp8 (uint8 E4M3 codes) and
+    paged_attn_prefill_fp8 is called."""
+    torch = _torch()
+    desc = _desc_of(k_cache)
+    if desc.num_kv_heads != num_kv_heads:
+        raise ValueError("num_kv_heads does not match the cache")
+    tq, num_heads, hs = q.shape
+    if hs != HEAD_SIZE or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must be [num_query_tokens, num_heads, 128]")
+    num_seqs, mbps = block_tables.shape
+    if tuple(query_start.shape) != (num_seqs + 1,) or tuple(context_lens.shape) != (num_seqs,):
+        raise ValueError("query_start must be [num_seqs + 1] and context_lens [num_seqs]")
+    fp8 = desc.dtype == PKV_FP8_E4M3
+    if fp8 != (k_scale is not None and v_scale is not None):
+        raise ValueError("an fp8 cache needs k_scale and v_scale, a 16-bit cache takes neither")
+    cache_dtype = torch.uint8 if fp8 else q.dtype
+    need = prefill_workspace_size(num_seqs, num_heads, mbps, tq, max_query_len, desc, partition_tokens)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = _gpu(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    args = [_gpu(out, "out", q.dtype, 3), _gpu(q, "q", None, 3), _gpu(k_cache, "k_cache", cache_dtype),
+            _gpu(v_cache, "v_cache", cache_dtype), _gpu(block_tables, "block_tables", torch.int32, 2),
+            _gpu(context_lens, "context_lens", torch.int32, 1), _gpu(query_start, "query_start", torch.int32, 1),
+            float(scale), int(num_kv_heads), int(num_seqs), int(num_heads), int(mbps), int(tq), int(max_query_len),
+            ctypes.byref(desc)]
+    if fp8:
+        sc = fp8_scales(q.dtype, k_scale, v_scale)
+        st = lib().paged_attn_prefill_fp8(*args, ctypes.byref(sc), int(partition_tokens), ws_ptr, ws_bytes,
+                                          _stream_handle(stream))
+    else:
+        st = lib().paged_attn_prefill(*args, int(partition_tokens), ws_ptr, ws_bytes, _stream_handle(stream))
+    _check(st, "paged_attn_prefill" + ("_fp8" if fp8 else ""))
+    return out
+
+
 def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, stream=None):
     """Write k[i], v[i] ([num_kv_heads, 128]) of every token i to slot_mapping[i]."""
     torch = _torch()
@@ -505,6 +562,7 @@ __all__ = [
     "lib", "status_string", "version", "cache_desc", "allocate_cache", "k_index", "v_index",
     "workspace_size", "partition_tokens_for", "paged_attn_decode", "paged_attn_decode_plan",
     "paged_attn_decode_run", "reshape_and_cache", "copy_blocks", "PKV_FP8_E4M3", "Fp8Scales", "fp8_scales",
-    "paged_attn_decode_fp8", "paged_attn_decode_run_fp8", "reshape_and_cache_fp8",
+    "paged_attn_decode_fp8", "paged_attn_decode_run_fp8", "reshape_and_cache_fp8", "paged_attn_prefill",
+    "prefill_workspace_size",
     "gather_cache", "BlockManager", "SIGNATURES",
 ]

@@ -399,6 +399,148 @@ pkv_status gather_cache(void* k_out, void* v_out, const void* k_cache, const voi
                                            is_fp8(cache), static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace and tiling of one prefill call.
+struct PrefillLayout {
+  int32_t hpt = 0, ppt = 0, q_blocks = 0, units = 0, group = 0, bpp = 0, parts = 0;
+  size_t partial_o = 0, partial_ml = 0, total = 0;
+};
+
+pkv_status prefill_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq, int32_t num_query_tokens,
+                          int32_t max_query_len, int32_t partition_tokens, const pkv_cache_desc* cache,
+                          PrefillLayout* out) {
+  pkv_status st = check_decode_shape(num_seqs, num_heads, max_blocks_per_seq, cache);
+  if (st != PKV_OK) return st;
+  if (num_query_tokens < 0 || max_query_len < 0) return PKV_ERR_INVALID;
+  if (num_query_tokens > 0 && (max_query_len < 1 || max_query_len > num_query_tokens)) return PKV_ERR_INVALID;
+  if (static_cast<int64_t>(max_query_len) > static_cast<int64_t>(max_blocks_per_seq) * pkv::kBlockSize)
+    return PKV_ERR_INVALID;
+  PrefillLayout P;
+  P.group = num_heads / cache->num_kv_heads;
+  P.hpt = P.group < 16 ? P.group : 16;
+  P.ppt = 16 / P.hpt;
+  const int32_t per_wg = pkv::kWavesPerGroup * P.ppt;
+  P.q_blocks = max_query_len > 0 ? (max_query_len + per_wg - 1) / per_wg : 0;
+  P.units = cache->num_kv_heads * ((P.group + 15) / 16);
+  // segment length: as for decode, with the work-groups of every query block
+  // counted as rows and the matrix-core kernels' residency
+  st = resolve_partition(num_seqs * (P.q_blocks > 0 ? P.q_blocks : 1), P.units, 2, PKV_BF16, max_blocks_per_seq,
+                         partition_tokens, &P.bpp, &P.parts);
+  if (st != PKV_OK) return st;
+  const int64_t items = static_cast<int64_t>(P.units) * num_seqs * P.q_blocks * P.parts;
+  if (items > (int64_t{1} << 31) - 64) return PKV_ERR_UNSUPPORTED;
+  size_t off = 0;
+  if (P.parts > 1) {
+    const size_t rows = static_cast<size_t>(num_query_tokens) * static_cast<size_t>(num_heads) *
+                        static_cast<size_t>(P.parts);
+    P.partial_o = off;
+    off += round_up(rows * pkv::kHeadSize * sizeof(float));
+    P.partial_ml = off;
+    off += round_up(rows * 2 * sizeof(float));
+  }
+  P.total = off;
+  *out = P;
+  return PKV_OK;
+}
+
+pkv_status prefill_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                        float scale, int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                        int32_t max_blocks_per_seq, int32_t num_query_tokens, int32_t max_query_len,
+                        const pkv_cache_desc* cache, const pkv_fp8_scales* fp8, int32_t partition_tokens,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status st = check_decode_shape(num_seqs, num_heads, max_blocks_per_seq, cache);
+  if (st != PKV_OK) return st;
+  if (is_fp8(cache) != (fp8 != nullptr)) return fp8 ? PKV_ERR_INVALID : PKV_ERR_UNSUPPORTED;
+  if (fp8) {
+    st = check_scales(fp8);
+    if (st != PKV_OK) return st;
+  }
+  if (num_kv_heads != cache->num_kv_heads) return PKV_ERR_INVALID;
+  if (!std::isfinite(scale)) return PKV_ERR_INVALID;
+  PrefillLayout P;
+  st = prefill_layout(num_seqs, num_heads, max_blocks_per_seq, num_query_tokens, max_query_len, partition_tokens,
+                      cache, &P);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0 || num_query_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start) return PKV_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID;
+  if (P.total > 0 && (!workspace || workspace_bytes < P.total || !aligned16(workspace))) return PKV_ERR_INVALID;
+
+  char* ws = static_cast<char*>(workspace);
+  pkv::PrefillArgs pa;
+  pkv::DecodeArgs& a = pa.d;
+  a.out = static_cast<uint16_t*>(out);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_o = P.parts > 1 ? reinterpret_cast<float*>(ws + P.partial_o) : nullptr;
+  a.ws_ml = P.parts > 1 ? reinterpret_cast<float*>(ws + P.partial_ml) : nullptr;
+  a.plan = nullptr;
+  a.scale_log2e = static_cast<float>(static_cast<double>(scale) * kLog2e * (fp8 ? static_cast<double>(fp8->k_scale) : 1.0));
+  a.out_scale = fp8 ? fp8->v_scale : 1.0f;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = P.group;
+  a.head_tiles = (P.group + 15) / 16;
+  a.units = P.units;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = cache->num_blocks;
+  a.blocks_per_part = P.bpp;
+  a.parts_max = P.parts;
+  a.planned = 0;
+  pa.query_start = query_start;
+  pa.heads_per_tile = P.hpt;
+  pa.pos_per_wave = P.ppt;
+  pa.q_blocks = P.q_blocks;
+  pa.num_query_tokens = num_query_tokens;
+  const int32_t act = fp8 ? fp8->act_dtype : cache->dtype;
+  return from_hip(pkv::launch_prefill(pa, act == PKV_F16 ? 0 : 1, fp8 != nullptr, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attn_prefill_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                         int32_t num_query_tokens, int32_t max_query_len, int32_t partition_tokens,
+                                         const pkv_cache_desc* cache) {
+  PrefillLayout P;
+  if (prefill_layout(num_seqs, num_heads, max_blocks_per_seq, num_query_tokens, max_query_len, partition_tokens,
+                     cache, &P) != PKV_OK)
+    return static_cast<size_t>(-1);
+  return P.total;
+}
+
+pkv_status paged_attn_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                              float scale, int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                              int32_t max_blocks_per_seq, int32_t num_query_tokens, int32_t max_query_len,
+                              const pkv_cache_desc* cache, int32_t partition_tokens, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale, num_kv_heads,
+                      num_seqs, num_heads, max_blocks_per_seq, num_query_tokens, max_query_len, cache, nullptr,
+                      partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pkv_status paged_attn_prefill_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* query_start, float scale, int32_t num_kv_heads, int32_t num_seqs,
+                                  int32_t num_heads, int32_t max_blocks_per_seq, int32_t num_query_tokens,
+                                  int32_t max_query_len, const pkv_cache_desc* cache, const pkv_fp8_scales* scales,
+                                  int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!scales) return PKV_ERR_INVALID;
+  return prefill_impl(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale, num_kv_heads,
+                      num_seqs, num_heads, max_blocks_per_seq, num_query_tokens, max_query_len, cache, scales,
+                      partition_tokens, workspace, workspace_bytes, stream);
+}
+
 const char* pkv_status_string(pkv_status s) {
   switch (s) {
     case PKV_OK: return "ok";

@@ -49,6 +49,20 @@ struct DecodeArgs {
   int planned;  // 1: items come from the plan's work list; 0: from blockIdx directly
 };
 
+// Chunked prefill: chunk query j of sequence s (output row query_start[s] + j)
+// sits at position context_lens[s] - C_s + j and attends to cache tokens
+// 0 .. that position.  A work-group takes 4 x 16 rows (query position, head) of
+// one KV head: wave w the positions [4 ppt qb + w ppt, + ppt) for heads_per_tile
+// heads each; all 4 waves stream the same blocks.
+struct PrefillArgs {
+  DecodeArgs d;                // out, q and the partials are per query token
+  const int32_t* query_start;  // [num_seqs + 1]
+  int heads_per_tile;          // hpt = min(group, 16)
+  int pos_per_wave;            // ppt = 16 / hpt
+  int q_blocks;                // ceil(max_query_len / (4 ppt))
+  int num_query_tokens;
+};
+
 struct PlanArgs {
   const int32_t* context_lens;
   int* plan;
@@ -63,6 +77,7 @@ struct PlanArgs {
 // act_dtype: 0 fp16, 1 bf16 (q, out); fp8_cache: the pages hold E4M3 codes
 hipError_t launch_decode(const DecodeArgs& a, int act_dtype, bool fp8_cache, hipStream_t stream);
 hipError_t launch_decode_plan(const PlanArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int act_dtype, bool fp8_cache, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                                     int32_t num_blocks, hipStream_t stream);

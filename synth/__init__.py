@@ -424,6 +424,9 @@ class PrefillWorkload:
     q: np.ndarray  # storage dtype [Tq, Hq, D]
     key_scales: Optional[np.ndarray] = None
     description: str = ""
+    kv_dtype: Optional[str] = None  # "fp8e4m3": the cache holds E4M3 codes of the rows
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -458,7 +461,8 @@ class PrefillWorkload:
 
 def make_prefill_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_heads: int, dtype: str,
                           context: Tuple[int, int], chunk: Tuple[int, int], key_scale=None, pool_slack: int = 4,
-                          name: str = "", description: str = "") -> PrefillWorkload:
+                          name: str = "", description: str = "", kv_dtype: Optional[str] = None,
+                          k_scale: float = 1.0, v_scale: float = 1.0) -> PrefillWorkload:
     """Contexts U[context], chunk lengths U[chunk] clipped to the context."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(context[0], context[1], num_seqs, endpoint=True).astype(np.int64)
@@ -471,7 +475,8 @@ def make_prefill_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_he
     q = _to_storage(rng.standard_normal((int(chunks.sum()), num_heads, HEAD_SIZE), dtype=np.float32), dtype)
     return PrefillWorkload(name=name or f"prefill{seed}", seed=seed, num_heads=num_heads, num_kv_heads=num_kv_heads,
                            dtype=dtype, context_lens=lens, chunk_lens=chunks, free_order=free_order, q=q,
-                           key_scales=key_scales, description=description)
+                           key_scales=key_scales, description=description, kv_dtype=kv_dtype, k_scale=k_scale,
+                           v_scale=v_scale)
 
 
 PREFILL_CONFIGS = {
