@@ -163,6 +163,68 @@ def copy_probe(mib: int, reps: int = 3):
     log(f"copy probe: {reps} copies of {mib} MiB")
 
 
+def prefill_bench(args, name: str) -> int:
+    """Chunked-prefill leg: one paged_attn_prefill call over a batch whose
+    chunks attend causally to their paged prefixes.  Roofline: the matrix
+    cores (4 * 128 flops per (query, visible key, head): QK and PV)."""
+    import numpy as np
+    import torch
+
+    import harness
+    import paged_kv_cache_345_amd as pkv
+    import synth
+
+    wl = synth.make_prefill(name)
+    log(f"workload {name}: {wl.description}")
+    pre = harness.build_prefill(wl, partition_tokens=args.partition_tokens or 0)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        pre.run()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for a, b in ev:
+        a.record()
+        pre.run()
+        b.record()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    log(f"prefill call avg {call_ms * 1e3:.1f} us")
+    L = wl.context_lens.astype(np.int64)
+    C = wl.chunk_lens.astype(np.int64)
+    visible = int(sum(int(((L[s] - C[s] + 1) + L[s]) * C[s] // 2) for s in range(wl.num_seqs)))  # sum of p + 1
+    flops = visible * 4 * 128 * wl.num_heads
+    kv_bytes = int(L.sum()) * 2 * wl.num_kv_heads * 128 * (1 if wl.kv_dtype == "fp8e4m3" else 2)
+    qo_bytes = 2 * int(C.sum()) * wl.num_heads * 128 * 2
+    tflops = flops / (call_ms * 1e-3) / 1e12
+    peak = 2500.0  # MI355X dense fp16 / bf16 matrix-core TFLOP/s
+    result = {
+        "metric": "chunked-prefill paged attention TFLOP/s (% of MI355X dense matrix-core peak) at 1 GPU",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.description, "name": name, "num_seqs": wl.num_seqs, "num_heads": wl.num_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_size": 128, "block_size": 16,
+                   "context_tokens": int(L.sum()), "query_tokens": int(C.sum()),
+                   "step": "paged_attn_prefill", "parallelism": "single GPU"},
+        "flops": flops,
+        "bytes": {"kv": kv_bytes, "q_out": qo_bytes},
+        "prefill_call_us": round(call_ms * 1e3, 2),
+        "query_tokens_per_s": round(int(C.sum()) / (call_ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "kernel": "paged_attn_prefill: prefill_kernel", "achieved": round(tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
+                     "hbm_gbs": round((kv_bytes + qo_bytes) / (call_ms * 1e-3) / 1e9, 1)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,6 +260,8 @@ def main() -> int:
         raise RuntimeError("bench.py needs a GPU")
     torch.cuda.set_device(0)
 
+    if args.workload in synth.PREFILL_CONFIGS:
+        return prefill_bench(args, args.workload)
     wl = synth.make_workload(args.workload)
     log(f"workload {wl.spec.name}: {wl.spec.description}")
     t0 = time.perf_counter()
