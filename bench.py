@@ -77,7 +77,8 @@ def step_bytes(wl, step):
 
 DECODE_SOURCES = ("paged_kv_cache_345_amd/csrc/decode.hip", "paged_kv_cache_345_amd/csrc/pkv_device.h",
                   "paged_kv_cache_345_amd/csrc/pkv_launch.h", "paged_kv_cache_345_amd/csrc/api.hip",
-                  "paged_kv_cache_345_amd/csrc/plan.hip")
+                  "paged_kv_cache_345_amd/csrc/plan.hip",
+                  "paged_kv_cache_345_amd/csrc/decode_common.h")
 
 
 def measured_traffic(workload: str):

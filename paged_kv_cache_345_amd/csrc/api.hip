@@ -425,11 +425,22 @@ pkv_status prefill_layout(int32_t num_seqs, int32_t num_heads, int32_t max_block
   const int32_t per_wg = pkv::kWavesPerGroup * P.ppt;
   P.q_blocks = max_query_len > 0 ? (max_query_len + per_wg - 1) / per_wg : 0;
   P.units = cache->num_kv_heads * ((P.group + 15) / 16);
-  // segment length: as for decode, with the work-groups of every query block
-  // counted as rows and the matrix-core kernels' residency
-  st = resolve_partition(num_seqs * (P.q_blocks > 0 ? P.q_blocks : 1), P.units, 2, PKV_BF16, max_blocks_per_seq,
-                         partition_tokens, &P.bpp, &P.parts);
-  if (st != PKV_OK) return st;
+  // Segment length.  Automatic: the whole key range (the smallest power of
+  // two of blocks covering max_blocks_per_seq) while the query blocks alone
+  // give every resident work-group two items, halved down to 16 blocks while
+  // they do not; every wave of a prefill work-group streams the whole segment.
+  if (partition_tokens == 0) {
+    const int64_t items = static_cast<int64_t>(num_seqs) * P.units * (P.q_blocks > 0 ? P.q_blocks : 1);
+    const int64_t want = 2 * resident_work_groups(2, PKV_BF16);
+    int32_t cover = 16;
+    while (cover < max_blocks_per_seq) cover *= 2;
+    P.bpp = cover;
+    while (P.bpp > 16 && items * ((max_blocks_per_seq + P.bpp - 1) / P.bpp) < want) P.bpp /= 2;
+    P.parts = (max_blocks_per_seq + P.bpp - 1) / P.bpp;
+  } else {
+    st = resolve_partition(num_seqs, P.units, 2, PKV_BF16, max_blocks_per_seq, partition_tokens, &P.bpp, &P.parts);
+    if (st != PKV_OK) return st;
+  }
   const int64_t items = static_cast<int64_t>(P.units) * num_seqs * P.q_blocks * P.parts;
   if (items > (int64_t{1} << 31) - 64) return PKV_ERR_UNSUPPORTED;
   size_t off = 0;
