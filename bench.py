@@ -226,6 +226,78 @@ def prefill_bench(args, name: str) -> int:
     return 0
 
 
+def swap_bench(args, name: str) -> int:
+    """Block-swap leg: every used block of the batch swapped out to a pinned
+    host pool (shuffled host slots), then back in to shuffled device blocks,
+    one swap_blocks call each.  Roofline: the host link (PCIe Gen5 x16, 64 GB/s
+    per direction); a contiguous device<->pinned copy of the same bytes by the
+    DMA engines is reported beside it."""
+    import numpy as np
+    import torch
+
+    import harness
+    import paged_kv_cache_345_amd as pkv
+    import synth
+
+    wl = synth.make_workload(name[len("swap_"):])
+    log(f"workload {name}: block swap of every used block of {wl.spec.name}")
+    step = harness.build_step(wl)
+    torch.cuda.synchronize()
+    tables = step.block_tables_host
+    used = np.unique(tables[tables >= 0]).astype(np.int32)
+    n = len(used)
+    rng = np.random.default_rng(0)
+    host_ids = rng.permutation(n).astype(np.int32)
+    dev_ids = rng.permutation(wl.pool_blocks)[:n].astype(np.int32)
+    shape = (n,) + tuple(step.k_cache.shape[1:])
+    hk = torch.empty(shape, dtype=step.k_cache.dtype, pin_memory=True)
+    hv = torch.empty(shape, dtype=step.k_cache.dtype, pin_memory=True)
+    out_pairs = torch.from_numpy(np.stack([used, host_ids], 1)).cuda()
+    in_pairs = torch.from_numpy(np.stack([host_ids, dev_ids], 1)).cuda()
+    k2, v2 = torch.empty_like(step.k_cache), torch.empty_like(step.v_cache)
+    nbytes = 2 * n * int(np.prod(shape[1:])) * step.k_cache.element_size()
+    flat_dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    flat_host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    K = max(1, args.steps // 10)
+    t_out = timed(lambda: pkv.swap_blocks(hk, hv, step.k_cache, step.v_cache, out_pairs), K)
+    t_in = timed(lambda: pkv.swap_blocks(k2, v2, hk, hv, in_pairs), K)
+    t_d2h = timed(lambda: flat_host.copy_(flat_dev, non_blocking=True), K)
+    t_h2d = timed(lambda: flat_dev.copy_(flat_host, non_blocking=True), K)
+    gbs = lambda ms: round(nbytes / (ms * 1e-3) / 1e9, 2)
+    log(f"{n} blocks, {nbytes / 1e9:.3f} GB: swap out {t_out:.3f} ms ({gbs(t_out)} GB/s), in {t_in:.3f} ms "
+        f"({gbs(t_in)} GB/s); contiguous DMA copy d2h {gbs(t_d2h)} GB/s, h2d {gbs(t_h2d)} GB/s")
+    peak = 64.0
+    result = {
+        "metric": "paged KV block swap GB/s (device <-> pinned host) at 1 GPU",
+        "value": gbs((t_out + t_in) / 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": 2,
+        "ms_per_step": round(t_out + t_in, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.kv_dtype, "data": "synthetic",
+        "config": {"workload": f"block swap of the {n} used blocks of: {wl.spec.description}", "name": name,
+                   "blocks": n, "bytes_per_direction": nbytes, "step": "swap_blocks out + swap_blocks in",
+                   "parallelism": "single GPU"},
+        "swap_out_gbs": gbs(t_out), "swap_in_gbs": gbs(t_in),
+        "dma_copy_gbs": {"d2h": gbs(t_d2h), "h2d": gbs(t_h2d)},
+        "roofline": {"bound": "host-link", "kernel": "swap_blocks_kernel", "achieved": gbs((t_out + t_in) / 2),
+                     "peak": peak, "unit": "GB/s", "frac": round(gbs((t_out + t_in) / 2) / peak, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +335,8 @@ def main() -> int:
 
     if args.workload in synth.PREFILL_CONFIGS:
         return prefill_bench(args, args.workload)
+    if args.workload.startswith("swap_"):
+        return swap_bench(args, args.workload)
     wl = synth.make_workload(args.workload)
     log(f"workload {wl.spec.name}: {wl.spec.description}")
     t0 = time.perf_counter()

@@ -189,6 +189,29 @@ pkv_status copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
                        const pkv_cache_desc* cache, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * swap_blocks — whole blocks moved between two caches of one shape (the
+ * number of blocks may differ), typically the device pool and a pool in pinned
+ * host memory ([stack] "把显存当虚拟内存管": blocks can be swapped out when
+ * device memory runs short, and back in).  For every pair (src, dst) block src
+ * of (src_k, src_v) — all Hkv pages of K and of V — is copied to block dst of
+ * (dst_k, dst_v).
+ *
+ *   dst_k/dst_v, src_k/src_v  device memory or pinned host memory (hipHostMalloc,
+ *                 torch pin_memory); the GPU reads and writes host memory through
+ *                 its device mapping, one launch for all pairs.  Pageable host
+ *                 memory and unknown pointers are refused with PKV_ERR_INVALID
+ *                 before anything is launched.
+ *   block_pairs   int32 [num_pairs, 2] (src, dst), device or pinned host memory;
+ *                 a pair with a block outside its pool is skipped; every dst
+ *                 distinct (else the copies race)
+ *   caches        same block_size, head_size, num_kv_heads and dtype
+ * Bit-exact.  num_pairs == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+pkv_status swap_blocks(void* dst_k, void* dst_v, const pkv_cache_desc* dst_cache, const void* src_k,
+                       const void* src_v, const pkv_cache_desc* src_cache, const int32_t* block_pairs,
+                       int32_t num_pairs, void* stream);
+
+/* ---------------------------------------------------------------------------
  * gather_cache — inspection helper: paged K/V of each sequence copied to a
  * contiguous [tokens, num_kv_heads, 128] array in logical token order.
  * Sequence s occupies rows out_offsets[s] .. out_offsets[s] + context_lens[s].

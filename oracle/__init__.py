@@ -15,8 +15,9 @@ What it computes, in float64 from the same fp16/bf16 values the GPU reads:
   share prompt blocks (page "vLLM 部署与 PagedAttention 原理 · 检索整理", item 2,
   the 2023 vLLM blog; page "vLLM：从 PagedAttention 长出来的开源服务栈", section
   "把显存当虚拟内存管").
-* ``scatter_ref`` / ``copy_ref`` — the slot-mapped cache write and the
-  copy-on-write block copy on a plain ``[num_blocks, block_size, Hkv, D]`` cache.
+* ``scatter_ref`` / ``copy_ref`` / ``swap_ref`` — the slot-mapped cache write,
+  the copy-on-write block copy and the block swap between two caches, on a
+  plain ``[num_blocks, block_size, Hkv, D]`` cache.
 * ``attention_ref`` / ``paged_decode_ref`` — decode attention: QK dot products,
   softmax normalisation and the weighted sum of V (page "vLLM 深度解析：以
   PagedAttention 与内核生态构建高吞吐 LLM 推理引擎", §2.1), read through the block
@@ -38,7 +39,7 @@ tests' docstrings).  No function is "parity unpinned".
 
 from .numerics import to_f64
 from .block_manager import BlockManager, OutOfBlocks
-from .cache_ops import new_cache, scatter_ref, copy_ref
+from .cache_ops import new_cache, scatter_ref, copy_ref, swap_ref
 from .attention import (
     attention_ref,
     paged_decode_ref,
@@ -57,6 +58,7 @@ __all__ = [
     "new_cache",
     "scatter_ref",
     "copy_ref",
+    "swap_ref",
     "attention_ref",
     "paged_decode_ref",
     "brute_force_ref",

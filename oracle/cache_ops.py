@@ -38,3 +38,15 @@ def copy_ref(k_cache, v_cache, block_pairs):
     for src, dst in np.asarray(block_pairs).reshape(-1, 2).tolist():
         k_cache[dst] = k_cache[src]
         v_cache[dst] = v_cache[src]
+
+
+def swap_ref(dst_k, dst_v, src_k, src_v, block_pairs):
+    """Block swap between two caches of one shape (page "vLLM：从 PagedAttention
+    长出来的开源服务栈", section "把显存当虚拟内存管": blocks can be swapped out of
+    device memory and back in): for each (src, dst), block src of the source
+    cache — every offset and head, K and V — becomes block dst of the
+    destination cache.  Pairs naming a block outside its cache are skipped."""
+    for src, dst in np.asarray(block_pairs).reshape(-1, 2).tolist():
+        if 0 <= src < src_k.shape[0] and 0 <= dst < dst_k.shape[0]:
+            dst_k[dst] = src_k[src]
+            dst_v[dst] = src_v[src]

@@ -87,6 +87,7 @@ SIGNATURES = {
     "paged_attn_decode_run_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _SP,
                                          _i32, _vp, _sz, _vp]),
     "copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _DP, _vp]),
+    "swap_blocks": (_i32, [_vp, _vp, _DP, _vp, _vp, _DP, _vp, _i32, _vp]),
     "gather_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _DP, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_version": (ctypes.c_char_p, []),
@@ -447,6 +448,30 @@ def copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
     _check(st, "copy_blocks")
 
 
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, *, stream=None):
+    """Copy block src of (src_k, src_v) to block dst of (dst_k, dst_v) for every
+    (src, dst) row of block_pairs; either side may be a pinned host tensor
+    (torch pin_memory), which the GPU reaches through its device mapping."""
+    torch = _torch()
+    dd, sd = _desc_of(dst_k), _desc_of(src_k)
+    for t, name, dt in ((dst_k, "dst_k", None), (dst_v, "dst_v", dst_k.dtype), (src_k, "src_k", dst_k.dtype),
+                        (src_v, "src_v", dst_k.dtype)):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+        if not t.is_contiguous() or (dt is not None and t.dtype != dt):
+            raise ValueError(f"{name} must be contiguous and of one dtype with dst_k")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2 or block_pairs.dtype != torch.int32:
+        raise ValueError("block_pairs must be int32 [num_pairs, 2]")
+    if not (block_pairs.is_cuda or block_pairs.is_pinned()) or not block_pairs.is_contiguous():
+        raise ValueError("block_pairs must be contiguous, on the GPU or pinned")
+    n = int(block_pairs.shape[0])
+    if n == 0:
+        return
+    st = lib().swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), ctypes.byref(dd), src_k.data_ptr(), src_v.data_ptr(),
+                           ctypes.byref(sd), block_pairs.data_ptr(), n, _stream_handle(stream))
+    _check(st, "swap_blocks")
+
+
 def gather_cache(k_out, v_out, k_cache, v_cache, block_tables, context_lens, out_offsets, *, stream=None):
     """Paged K/V of every sequence into contiguous [tokens, num_kv_heads, 128]."""
     torch = _torch()
@@ -563,6 +588,6 @@ __all__ = [
     "workspace_size", "partition_tokens_for", "paged_attn_decode", "paged_attn_decode_plan",
     "paged_attn_decode_run", "reshape_and_cache", "copy_blocks", "PKV_FP8_E4M3", "Fp8Scales", "fp8_scales",
     "paged_attn_decode_fp8", "paged_attn_decode_run_fp8", "reshape_and_cache_fp8", "paged_attn_prefill",
-    "prefill_workspace_size",
+    "prefill_workspace_size", "swap_blocks",
     "gather_cache", "BlockManager", "SIGNATURES",
 ]

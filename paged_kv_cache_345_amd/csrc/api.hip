@@ -552,6 +552,61 @@ pkv_status paged_attn_prefill_fp8(void* out, const void* q, const void* k_cache,
                       partition_tokens, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The address a kernel on the current device uses for p: p itself for device
+// memory, the device mapping for pinned host memory.  Anything else (pageable
+// host memory, unknown pointers) is refused, so no kernel ever touches an
+// address the device cannot reach.
+pkv_status device_address(const void* p, const void** out) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the error this query leaves behind
+    return PKV_ERR_INVALID;
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    *out = p;
+    return PKV_OK;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr) {
+    *out = attr.devicePointer;
+    return PKV_OK;
+  }
+  return PKV_ERR_INVALID;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status swap_blocks(void* dst_k, void* dst_v, const pkv_cache_desc* dst_cache, const void* src_k,
+                       const void* src_v, const pkv_cache_desc* src_cache, const int32_t* block_pairs,
+                       int32_t num_pairs, void* stream) {
+  pkv_status st = check_desc(dst_cache);
+  if (st != PKV_OK) return st;
+  st = check_desc(src_cache);
+  if (st != PKV_OK) return st;
+  if (dst_cache->num_kv_heads != src_cache->num_kv_heads || dst_cache->dtype != src_cache->dtype)
+    return PKV_ERR_INVALID;
+  if (num_pairs < 0) return PKV_ERR_INVALID;
+  if (num_pairs == 0) return PKV_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !block_pairs) return PKV_ERR_INVALID;
+  if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v)) return PKV_ERR_INVALID;
+  if (static_cast<int64_t>(num_pairs) * 2 * src_cache->num_kv_heads > INT32_MAX) return PKV_ERR_INVALID;
+  const void* p[5] = {dst_k, dst_v, src_k, src_v, block_pairs};
+  const void* d[5];
+  for (int i = 0; i < 5; ++i) {
+    st = device_address(p[i], &d[i]);
+    if (st != PKV_OK) return st;
+  }
+  return from_hip(pkv::launch_swap_blocks(const_cast<void*>(d[0]), const_cast<void*>(d[1]), dst_cache->num_blocks, d[2],
+                                          d[3], src_cache->num_blocks, static_cast<const int32_t*>(d[4]), num_pairs,
+                                          src_cache->num_kv_heads, page_bytes(src_cache),
+                                          static_cast<hipStream_t>(stream)));
+}
+
 const char* pkv_status_string(pkv_status s) {
   switch (s) {
     case PKV_OK: return "ok";

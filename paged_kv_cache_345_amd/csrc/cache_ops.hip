@@ -136,6 +136,31 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_c
   store16<kNonTemporal>(range_rsrc(d, page_bytes), 16u * threadIdx.x, s[threadIdx.x]);
 }
 
+// Block swap between two caches (typically the device pool and a pool in
+// pinned host memory, reached through its device mapping): one work-group per
+// page, 16 bytes per thread; the work-group index -> (pair, which of the
+// 2*Hkv pages of the block).  Pairs with a block outside its own pool are
+// skipped.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(char* __restrict__ dst_k, char* __restrict__ dst_v,
+                                                          int32_t dst_blocks, const char* __restrict__ src_k,
+                                                          const char* __restrict__ src_v, int32_t src_blocks,
+                                                          const int32_t* __restrict__ block_pairs, int num_kv_heads,
+                                                          int page_bytes) {
+  const int64_t wg = blockIdx.x;
+  const int pages = 2 * num_kv_heads;
+  const int64_t pair = wg / pages;
+  const int page = static_cast<int>(wg - pair * pages);
+  const int32_t src = block_pairs[2 * pair];
+  const int32_t dst = block_pairs[2 * pair + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const bool is_k = page < num_kv_heads;
+  const int h = is_k ? page : page - num_kv_heads;
+  const uint4* s = reinterpret_cast<const uint4*>((is_k ? src_k : src_v) +
+                                                  (static_cast<int64_t>(src) * num_kv_heads + h) * page_bytes);
+  uint4* d = reinterpret_cast<uint4*>((is_k ? dst_k : dst_v) + (static_cast<int64_t>(dst) * num_kv_heads + h) * page_bytes);
+  d[threadIdx.x] = s[threadIdx.x];
+}
+
 // One work-group per (sequence, logical block).  Thread -> (token, head, chunk).
 __global__ __launch_bounds__(256) void gather_cache_kernel(
     uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, const uint16_t* __restrict__ k_cache,
@@ -250,6 +275,16 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block
   const int64_t grid = static_cast<int64_t>(num_pairs) * 2 * num_kv_heads;
   copy_blocks_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(page_bytes / 16), 0, stream>>>(
       static_cast<char*>(k_cache), static_cast<char*>(v_cache), block_pairs, num_kv_heads, num_blocks, page_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(void* dst_k, void* dst_v, int32_t dst_blocks, const void* src_k, const void* src_v,
+                              int32_t src_blocks, const int32_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                              int32_t page_bytes, hipStream_t stream) {
+  const int64_t grid = static_cast<int64_t>(num_pairs) * 2 * num_kv_heads;
+  swap_blocks_kernel<<<dim3(static_cast<uint32_t>(grid)), dim3(page_bytes / 16), 0, stream>>>(
+      static_cast<char*>(dst_k), static_cast<char*>(dst_v), dst_blocks, static_cast<const char*>(src_k),
+      static_cast<const char*>(src_v), src_blocks, block_pairs, num_kv_heads, page_bytes);
   return hipGetLastError();
 }
 

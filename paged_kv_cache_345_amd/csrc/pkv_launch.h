@@ -87,6 +87,9 @@ hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_ca
                                         hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
                               int32_t num_kv_heads, int32_t num_blocks, int32_t page_bytes, hipStream_t stream);
+hipError_t launch_swap_blocks(void* dst_k, void* dst_v, int32_t dst_blocks, const void* src_k, const void* src_v,
+                              int32_t src_blocks, const int32_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                              int32_t page_bytes, hipStream_t stream);
 hipError_t launch_gather_cache(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                int32_t max_blocks_per_seq, const int32_t* out_offsets, int32_t num_kv_heads,

@@ -110,3 +110,26 @@ def test_copy_on_write_step_values():
                 assert np.array_equal(st.k_cache[b], st.k_cache_before_step[b])
         for s in range(wl.num_seqs):
             assert np.abs(st.out[s] - _contiguous_ref(wl, s)).max() <= 1e-12
+
+
+def test_swap_ref_round_trip_and_copy_special_case():
+    """Swapping blocks out to a second cache and back with the inverse pairs
+    restores them; swapping within one cache is the block copy."""
+    rng = np.random.default_rng(77)
+    a_k = rng.integers(0, 1 << 16, (6, 16, 2, 8)).astype(np.uint16)
+    a_v = rng.integers(0, 1 << 16, (6, 16, 2, 8)).astype(np.uint16)
+    b_k, b_v = np.zeros((4, 16, 2, 8), np.uint16), np.zeros((4, 16, 2, 8), np.uint16)
+    out_pairs = np.array([[5, 0], [1, 3], [2, 1]])
+    oracle.swap_ref(b_k, b_v, a_k, a_v, out_pairs)
+    back_k, back_v = np.zeros_like(a_k), np.zeros_like(a_v)
+    oracle.swap_ref(back_k, back_v, b_k, b_v, out_pairs[:, ::-1])
+    for src, _dst in out_pairs:
+        assert np.array_equal(back_k[src], a_k[src]) and np.array_equal(back_v[src], a_v[src])
+    assert not back_k[0].any() and not back_k[3].any()  # untouched
+    c_k, c_v = a_k.copy(), a_v.copy()
+    d_k, d_v = a_k.copy(), a_v.copy()
+    pairs = np.array([[0, 4], [2, 3]])
+    oracle.swap_ref(c_k, c_v, c_k, c_v, pairs)
+    oracle.copy_ref(d_k, d_v, pairs)
+    assert np.array_equal(c_k, d_k) and np.array_equal(c_v, d_v)
+    oracle.swap_ref(b_k, b_v, a_k, a_v, np.array([[9, 0], [0, 7]]))  # out-of-range pairs skipped
