@@ -371,14 +371,45 @@ pkv_status pkv_bm_free(pkv_block_manager* bm, int32_t seq);
  * int32 [n] or NULL.  PKV_ERR_INVALID if a sequence has more than max_blocks. */
 pkv_status pkv_bm_block_table(const pkv_block_manager* bm, const int32_t* seqs, int32_t n,
                               int32_t max_blocks, int32_t* table_out, int32_t* context_lens_out);
+/* blocks available to new allocations: the free list plus the evictable blocks
+ * of the prefix cache */
 int32_t pkv_bm_num_free(const pkv_block_manager* bm);
 int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);   /* -1 if out of range */
 int32_t pkv_bm_length(const pkv_block_manager* bm, int32_t seq);       /* -1 if unknown */
 int32_t pkv_bm_num_seq_blocks(const pkv_block_manager* bm, int32_t seq); /* -1 if unknown */
 /* allocated-but-unused slots of one sequence (at most 15); -1 if unknown */
 int32_t pkv_bm_waste(const pkv_block_manager* bm, int32_t seq);
-/* free list contents front to back: host int32 [capacity]; returns the count */
+/* free list contents front to back (evictable blocks not included): host int32
+ * [capacity]; returns the free list's length */
 int32_t pkv_bm_free_list(const pkv_block_manager* bm, int32_t* out, int32_t capacity);
+
+/* Prefix caching across requests ([repo] §2.2: the KV cache of an identical
+ * prefix, such as a system prompt, is computed once and reused by later
+ * requests; the policy below is this library's reading).
+ *   - A full block whose token ids are known is registered under the key
+ *     (its chain's previous block, its 16 token ids); the key of a block thus
+ *     names its whole token prefix.  Only full blocks are registered.
+ *   - add_cached: a new sequence with token_ids (host int32 [num_tokens])
+ *     reuses the longest run of registered full blocks matching its first
+ *     tokens (refcount + 1), takes fresh blocks for the rest, registers its
+ *     fresh full blocks, and reports in num_cached_out the tokens whose K/V are
+ *     already in the cache (a multiple of 16: only the other tokens need the
+ *     slot-mapped write); slots_out as for pkv_bm_add.
+ *   - append_token: append_slot for a token with a known id; the block it
+ *     completes is registered (unless that content is registered already).
+ *     pkv_bm_append_slot / pkv_bm_step append tokens without ids: a
+ *     sequence's blocks after such a token are never registered.
+ *   - A registered block whose refcount drops to 0 is evictable, not free: a
+ *     later hit revives it; allocations take free-list blocks first and then
+ *     evict the least recently freed evictable block, dropping its key.
+ *   - Sequences added with pkv_bm_add register nothing: without add_cached /
+ *     append_token the manager behaves exactly as described above.
+ * Errors and all-or-nothing behaviour as for the other calls. */
+pkv_status pkv_bm_add_cached(pkv_block_manager* bm, int32_t seq, int32_t num_tokens, const int32_t* token_ids,
+                             int32_t* slots_out, int32_t* num_cached_out);
+pkv_status pkv_bm_append_token(pkv_block_manager* bm, int32_t seq, int32_t token_id, int32_t* slot_out,
+                               int32_t* cow_pair_out);
+int32_t pkv_bm_num_evictable(const pkv_block_manager* bm);
 
 #ifdef __cplusplus
 }

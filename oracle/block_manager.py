@@ -23,9 +23,30 @@ Readings where the pages are silent:
   old block's count drops by one — so the last of the sharing samples to append
   keeps the original block and writes into it in place;
 * a slot is ``physical_block * block_size + offset``.
+
+Prefix caching (page "vLLM 深度解析：以 PagedAttention 与内核生态构建高吞吐 LLM
+推理引擎", §2.2: the cache of an identical prefix, such as a shared system
+prompt, is computed once and reused by later requests).  The page gives the
+purpose, not the policy; the reading taken here:
+
+* a full block whose token ids are known is registered in a table under the
+  pair (node of the previous block of its chain, its token ids); node ids are
+  drawn from a counter that never repeats, 0 standing for "no previous block",
+  so a key names one whole token prefix;
+* ``add_cached`` walks the new prompt's full blocks through that table and
+  reuses the longest matching run (reference count + 1); the rest are fresh
+  blocks, and fresh full blocks are registered;
+* ``append_token`` is ``append_slot`` for a token whose id is known; the block
+  it fills is registered, unless a block with that key exists already (then
+  the chain follows the existing block's node and this block stays private);
+  a token appended without an id (``append_slot``, ``step``) ends registration
+  for the rest of that sequence;
+* a registered block whose count drops to 0 is "evictable": it keeps its key,
+  a later hit revives it, and allocation takes it (least recently freed first,
+  dropping its key) only once the free list is empty.
 """
 
-from collections import deque
+from collections import OrderedDict, deque
 from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -49,13 +70,49 @@ class BlockManager:
         self.ref: List[int] = [0] * num_blocks
         self.blocks: Dict[int, List[int]] = {}
         self.length: Dict[int, int] = {}
+        # prefix cache
+        self.table: Dict[Tuple[int, Tuple[int, ...]], int] = {}  # key -> block
+        self.key: Dict[int, Tuple[int, Tuple[int, ...]]] = {}    # block -> its key
+        self.node: Dict[int, int] = {}                           # block -> node id
+        self.evictable: "OrderedDict[int, None]" = OrderedDict()  # least recently freed first
+        self.chain: Dict[int, Optional[int]] = {}  # seq -> node of its last full block (None: ids unknown)
+        self.pending: Dict[int, List[int]] = {}    # seq -> token ids of its partial last block
+        self._next_node = 1
 
     # ------------------------------------------------------------------
     def _take(self) -> int:
-        b = self.free.popleft()
+        if self.free:
+            b = self.free.popleft()
+        else:  # evict the least recently freed registered block
+            b, _ = self.evictable.popitem(last=False)
+            del self.table[self.key.pop(b)]
+            del self.node[b]
         assert self.ref[b] == 0
         self.ref[b] = 1
         return b
+
+    def _release(self, b: int) -> None:
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            if b in self.key:
+                self.evictable[b] = None
+            else:
+                self.free.append(b)
+
+    def _filled(self, seq: int, b: int, tokens: Sequence[int]) -> None:
+        """Block b of ``seq`` now holds ``tokens`` (a whole block): register it."""
+        parent = self.chain[seq]
+        if parent is None:
+            return
+        k = (parent, tuple(int(t) for t in tokens))
+        if k in self.table:
+            self.chain[seq] = self.node[self.table[k]]
+            return
+        self.table[k] = b
+        self.key[b] = k
+        self.node[b] = self._next_node
+        self.chain[seq] = self._next_node
+        self._next_node += 1
 
     def _slot(self, seq: int, pos: int) -> int:
         bs = self.block_size
@@ -69,11 +126,47 @@ class BlockManager:
         if num_tokens < 0:
             raise ValueError("negative token count")
         need = -(-num_tokens // self.block_size)
-        if need > len(self.free):
-            raise OutOfBlocks(f"need {need} blocks, {len(self.free)} free")
+        if need > self.num_free():
+            raise OutOfBlocks(f"need {need} blocks, {self.num_free()} free")
         self.blocks[seq] = [self._take() for _ in range(need)]
         self.length[seq] = num_tokens
+        self.chain[seq] = None
+        self.pending[seq] = []
         return [self._slot(seq, t) for t in range(num_tokens)]
+
+    def add_cached(self, seq: int, token_ids: Sequence[int]) -> Tuple[List[int], int]:
+        """New sequence with these token ids, reusing the registered blocks of
+        its longest cached prefix.  Returns (slots, tokens already cached)."""
+        if seq in self.blocks:
+            raise ValueError(f"sequence {seq} exists")
+        ids = [int(t) for t in token_ids]
+        bs = self.block_size
+        full = len(ids) // bs
+        hits, parent = [], 0
+        while len(hits) < full:
+            j = len(hits)
+            b = self.table.get((parent, tuple(ids[j * bs:(j + 1) * bs])))
+            if b is None:
+                break
+            hits.append(b)
+            parent = self.node[b]
+        need = -(-len(ids) // bs) - len(hits)
+        avail = self.num_free() - sum(1 for b in hits if b in self.evictable)
+        if need > avail:
+            raise OutOfBlocks(f"need {need} blocks, {avail} available")
+        for b in hits:
+            self.evictable.pop(b, None)
+            self.ref[b] += 1
+        self.blocks[seq] = list(hits)
+        self.chain[seq] = parent
+        for j in range(len(hits), len(hits) + need):
+            b = self._take()
+            self.blocks[seq].append(b)
+            if j < full:
+                self._filled(seq, b, ids[j * bs:(j + 1) * bs])
+        self.length[seq] = len(ids)
+        self.pending[seq] = ids[full * bs:]
+        return [self._slot(seq, t) for t in range(len(ids))], len(hits) * bs
 
     def fork(self, parent: int, child: int) -> None:
         """``child`` shares every block of ``parent`` (reference count +1)."""
@@ -84,6 +177,8 @@ class BlockManager:
             self.ref[b] += 1
         self.blocks[child] = list(blocks)
         self.length[child] = self.length[parent]
+        self.chain[child] = self.chain[parent]
+        self.pending[child] = list(self.pending[parent])
 
     def append_slot(self, seq: int) -> Tuple[int, Optional[Tuple[int, int]]]:
         """Room for one more token; returns (slot, copy pair or None)."""
@@ -92,20 +187,34 @@ class BlockManager:
         blocks = self.blocks[seq]
         cow = None
         if pos % bs == 0:
-            if not self.free:
+            if not self.num_free():
                 raise OutOfBlocks("no free block for a new token")
             blocks.append(self._take())
         else:
             old = blocks[pos // bs]
             if self.ref[old] > 1:
-                if not self.free:
+                if not self.num_free():
                     raise OutOfBlocks("no free block for copy-on-write")
                 new = self._take()
                 self.ref[old] -= 1
                 blocks[pos // bs] = new
                 cow = (old, new)
         self.length[seq] = pos + 1
+        self.chain[seq] = None  # a token without an id
+        self.pending[seq] = []
         return self._slot(seq, pos), cow
+
+    def append_token(self, seq: int, token_id: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+        """``append_slot`` for a token whose id is known (prefix caching)."""
+        chain, pend = self.chain[seq], self.pending[seq]
+        slot, cow = self.append_slot(seq)
+        if chain is not None:
+            self.chain[seq] = chain
+            self.pending[seq] = pend + [int(token_id)]
+            if len(self.pending[seq]) == self.block_size:
+                self._filled(seq, self.blocks[seq][-1], self.pending[seq])
+                self.pending[seq] = []
+        return slot, cow
 
     def step(self, seqs: Iterable[int]) -> Tuple[np.ndarray, np.ndarray]:
         """One decode step: append a token to each sequence, in order.
@@ -127,8 +236,8 @@ class BlockManager:
                 if r > 1:
                     need += 1
                     pending_ref[b] = r - 1
-        if need > len(self.free):
-            raise OutOfBlocks(f"step needs {need} blocks, {len(self.free)} free")
+        if need > self.num_free():
+            raise OutOfBlocks(f"step needs {need} blocks, {self.num_free()} free")
         slots, pairs = [], []
         for s in seqs:
             slot, cow = self.append_slot(s)
@@ -140,10 +249,8 @@ class BlockManager:
 
     def free_seq(self, seq: int) -> None:
         for b in self.blocks.pop(seq):
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
-        del self.length[seq]
+            self._release(b)
+        del self.length[seq], self.chain[seq], self.pending[seq]
 
     # ------------------------------------------------------------------
     def block_table(self, seqs: Sequence[int], max_blocks: int) -> np.ndarray:
@@ -164,7 +271,11 @@ class BlockManager:
         return self.block_size * len(self.blocks[seq]) - self.length[seq]
 
     def num_free(self) -> int:
-        return len(self.free)
+        """Blocks an allocation can take: the free list and the evictable blocks."""
+        return len(self.free) + len(self.evictable)
+
+    def num_evictable(self) -> int:
+        return len(self.evictable)
 
     def num_used(self) -> int:
-        return self.num_blocks - len(self.free)
+        return self.num_blocks - self.num_free()

@@ -105,6 +105,9 @@ SIGNATURES = {
     "pkv_bm_num_seq_blocks": (_i32, [_vp, _i32]),
     "pkv_bm_waste": (_i32, [_vp, _i32]),
     "pkv_bm_free_list": (_i32, [_vp, _i32p, _i32]),
+    "pkv_bm_add_cached": (_i32, [_vp, _i32, _i32, _i32p, _i32p, _i32p]),
+    "pkv_bm_append_token": (_i32, [_vp, _i32, _i32, _i32p, _i32p]),
+    "pkv_bm_num_evictable": (_i32, [_vp]),
 }
 
 _LIB = None
@@ -576,10 +579,33 @@ class BlockManager:
         return int(lib().pkv_bm_waste(self._h, int(seq)))
 
     def free_list(self) -> np.ndarray:
+        """The free list, front to back (evictable prefix-cache blocks not included)."""
         n = self.num_free()
         out = np.empty(max(n, 1), dtype=np.int32)
-        lib().pkv_bm_free_list(self._h, _p(out), n)
-        return out[:n].copy()
+        m = lib().pkv_bm_free_list(self._h, _p(out), n)
+        return out[:m].copy()
+
+    # prefix caching
+    def add_cached(self, seq: int, token_ids) -> Tuple[np.ndarray, int]:
+        """New sequence with these token ids, reusing registered full blocks of
+        its prefix: (slots, number of tokens already cached)."""
+        ids = _i32_array(token_ids)
+        n = int(ids.shape[0])
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        cached = np.zeros(1, dtype=np.int32)
+        _check(lib().pkv_bm_add_cached(self._h, int(seq), n, _p(ids) if n else None, _p(slots), _p(cached)),
+               "pkv_bm_add_cached")
+        return slots[:n].copy(), int(cached[0])
+
+    def append_token(self, seq: int, token_id: int):
+        slot = np.zeros(1, dtype=np.int32)
+        pair = np.zeros(2, dtype=np.int32)
+        _check(lib().pkv_bm_append_token(self._h, int(seq), int(token_id), _p(slot), _p(pair)),
+               "pkv_bm_append_token")
+        return int(slot[0]), (None if pair[0] < 0 else (int(pair[0]), int(pair[1])))
+
+    def num_evictable(self) -> int:
+        return int(lib().pkv_bm_num_evictable(self._h))
 
 
 __all__ = [

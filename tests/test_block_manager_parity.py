@@ -114,3 +114,99 @@ def test_invalid_calls_leave_state():
     assert cpp.num_free() == 2 and cpp.length(7) == 20
     with pytest.raises(ValueError):
         pkv.BlockManager(4, BS, [0, 1, 1, 2])
+
+
+def _compare_prefix_state(cpp, ref, seqs):
+    _compare_state(cpp, ref, seqs)
+    assert cpp.num_evictable() == ref.num_evictable()
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_prefix_cache_ops_identical(seed):
+    """Random streams mixing prompts that share prefixes (add_cached), generated
+    tokens with ids (append_token), tokens without ids, forks, frees and steps:
+    identical slots, cached-token counts, copy pairs, free lists, evictable
+    counts, refcounts and block tables."""
+    rng = np.random.default_rng(100 + seed)
+    nb = int(rng.integers(6, 50))
+    order = rng.permutation(nb)
+    cpp = pkv.BlockManager(nb, BS, order)
+    ref = oracle.BlockManager(nb, BS, order)
+    bases = [rng.integers(0, 3, 90).tolist() for _ in range(3)]
+    live, nxt = [], 0
+    for _ in range(300):
+        op = int(rng.integers(0, 10))
+        if op <= 1 or not live:
+            n = int(rng.integers(0, 70))
+            base = bases[int(rng.integers(0, 3))]
+            k = int(rng.integers(0, min(n, len(base)) + 1))
+            ids = base[:k] + rng.integers(0, 4, n - k).tolist()
+            if op == 1 and rng.random() < 0.3:
+                try:
+                    want = ref.add(nxt, n)
+                except oracle.OutOfBlocks:
+                    with pytest.raises(pkv.OutOfBlocks):
+                        cpp.add(nxt, n)
+                    continue
+                assert cpp.add(nxt, n).tolist() == want
+            else:
+                try:
+                    want, wc = ref.add_cached(nxt, ids)
+                except oracle.OutOfBlocks:
+                    with pytest.raises(pkv.OutOfBlocks):
+                        cpp.add_cached(nxt, ids)
+                    continue
+                got, gc = cpp.add_cached(nxt, ids)
+                assert got.tolist() == want and gc == wc
+            live.append(nxt)
+            nxt += 1
+        elif op == 2:
+            p = int(rng.choice(live))
+            ref.fork(p, nxt)
+            cpp.fork(p, nxt)
+            live.append(nxt)
+            nxt += 1
+        elif op == 3 and len(live) > 1:
+            s = int(rng.choice(live))
+            ref.free_seq(s)
+            cpp.free_seq(s)
+            live.remove(s)
+        elif op == 9:
+            seqs = [int(x) for x in rng.choice(live, size=min(len(live), 3), replace=False)]
+            try:
+                slots, pairs = ref.step(seqs)
+            except oracle.OutOfBlocks:
+                with pytest.raises(pkv.OutOfBlocks):
+                    cpp.step(seqs)
+                continue
+            cs, cp = cpp.step(seqs)
+            assert np.array_equal(cs, slots) and np.array_equal(cp, pairs)
+        else:
+            s = int(rng.choice(live))
+            t = int(rng.integers(0, 3))
+            call = (lambda m: m.append_slot(s)) if op == 8 else (lambda m: m.append_token(s, t))
+            try:
+                want = call(ref)
+            except oracle.OutOfBlocks:
+                with pytest.raises(pkv.OutOfBlocks):
+                    call(cpp)
+                continue
+            assert call(cpp) == want
+        _compare_prefix_state(cpp, ref, live)
+
+
+def test_prefix_cache_invalid_calls_leave_state():
+    cpp = pkv.BlockManager(3, BS)
+    ids = list(range(40))
+    assert cpp.add_cached(0, ids)[1] == 0
+    with pytest.raises(pkv.PagedKVError):
+        cpp.add_cached(0, ids)  # duplicate id
+    with pytest.raises(pkv.PagedKVError):
+        cpp.append_token(5, 1)  # unknown sequence
+    cpp.free_seq(0)
+    assert cpp.num_free() == 3 and cpp.num_evictable() == 2 and cpp.free_list().tolist() == [2]
+    with pytest.raises(pkv.OutOfBlocks):
+        cpp.add_cached(1, ids + list(range(500, 540)))  # 2 revived + 3 fresh > 3
+    assert cpp.num_free() == 3 and cpp.num_evictable() == 2
+    slots, c = cpp.add_cached(1, ids)
+    assert c == 32 and slots[:32].tolist() == list(range(32))
