@@ -298,6 +298,149 @@ def swap_bench(args, name: str) -> int:
     return 0
 
 
+def prefix_bench(args, name: str) -> int:
+    """Prefix-cache leg: admission of a batch of new prompts that share a
+    system prompt already in the cache.  With prefix caching the block manager
+    (add_cached) hands back the shared blocks, only the own tokens are written
+    (reshape_and_cache) and only they are evaluated (paged_attn_prefill,
+    attending to the cached prefix); without it every prompt token is written
+    and evaluated.  Both GPU paths are timed with HIP events, and the host
+    manager's calls with the wall clock.  Roofline: the prefill kernel of the
+    cached path on the matrix cores (4 * 128 flops per (query, visible key,
+    head))."""
+    import numpy as np
+    import torch
+
+    import harness
+    import paged_kv_cache_345_amd as pkv
+    import synth
+
+    wl, desc = synth.make_prefix(name)
+    log(f"workload {name}: {desc}")
+    dev = "cuda"
+    reqs = list(range(wl.phase1, wl.num_requests))
+    prompts = {r: wl.prompt(r) for r in range(wl.num_requests)}
+
+    def admit(cached: bool):
+        bm = pkv.BlockManager(wl.pool_blocks, 16, wl.free_order)
+        for r in range(wl.phase1):  # the earlier requests that registered the system prompt
+            bm.add_cached(r, prompts[r][0]) if cached else bm.add(r, prompts[r][0].shape[0])
+        t0 = time.perf_counter()
+        res = {r: (bm.add_cached(r, prompts[r][0]) if cached else (bm.add(r, prompts[r][0].shape[0]), 0))
+               for r in reqs}
+        return bm, res, time.perf_counter() - t0
+
+    host = {}
+    for cached in (True, False):
+        times = [admit(cached)[2] for _ in range(5)]
+        host[cached] = min(times) / len(reqs) * 1e6
+    log(f"host admission: add_cached {host[True]:.1f} us/request, add {host[False]:.1f} us/request")
+
+    def build(cached: bool):
+        bm, res, _ = admit(cached)
+        k_cache, v_cache = pkv.allocate_cache(wl.pool_blocks, wl.num_kv_heads, harness.torch_dtype(wl.dtype), dev)
+        for r in range(wl.phase1):  # earlier requests' rows: written once, outside the timed step
+            bm_slots = bm.block_table([r], bm.num_seq_blocks(r))[0]
+            ids, k, v = prompts[r]
+            slots = np.array([bm_slots[t // 16] * 16 + t % 16 for t in range(ids.shape[0])], dtype=np.int32)
+            pkv.reshape_and_cache(harness.to_device(k, wl.dtype, dev), harness.to_device(v, wl.dtype, dev),
+                                  k_cache, v_cache, torch.from_numpy(slots).to(dev))
+        slots, ks, vs, qs_rows, ctx, first = [], [], [], [], [], []
+        for r in reqs:
+            sl, c = res[r]
+            ids, k, v = prompts[r]
+            L = ids.shape[0]
+            fp = min(c, L - 1)
+            slots.append(np.asarray(sl[c:], dtype=np.int32))
+            ks.append(k[c:])
+            vs.append(v[c:])
+            qs_rows.append(wl.q_rows(r)[fp:L])
+            ctx.append(L)
+            first.append(fp)
+        ctx = np.array(ctx, dtype=np.int64)
+        chunks = ctx - np.array(first, dtype=np.int64)
+        qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+        mb = max(bm.num_seq_blocks(r) for r in reqs)
+        d = dict(k=harness.to_device(np.concatenate(ks), wl.dtype, dev),
+                 v=harness.to_device(np.concatenate(vs), wl.dtype, dev),
+                 slots=torch.from_numpy(np.concatenate(slots)).to(dev),
+                 q=harness.to_device(np.concatenate(qs_rows), wl.dtype, dev),
+                 tables=torch.from_numpy(bm.block_table(reqs, mb)).to(dev),
+                 ctx=torch.from_numpy(ctx.astype(np.int32)).to(dev), qs=torch.from_numpy(qs).to(dev),
+                 max_q=int(chunks.max()), k_cache=k_cache, v_cache=v_cache, chunks=chunks, ctx_np=ctx,
+                 written=int(sum(x.shape[0] for x in slots)), hit=int(sum(res[r][1] for r in reqs)))
+        d["out"] = torch.empty_like(d["q"])
+        desc_ = pkv.cache_desc(wl.pool_blocks, wl.num_kv_heads, k_cache.dtype)
+        ws = pkv.prefill_workspace_size(len(reqs), wl.num_heads, mb, int(qs[-1]), d["max_q"], desc_)
+        d["ws"] = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+        return d
+
+    def step_fns(d):
+        w = lambda: pkv.reshape_and_cache(d["k"], d["v"], d["k_cache"], d["v_cache"], d["slots"])  # noqa: E731
+        a = lambda: pkv.paged_attn_prefill(d["out"], d["q"], d["k_cache"], d["v_cache"], d["tables"],  # noqa: E731
+                                           d["ctx"], d["qs"], wl.scale, wl.num_kv_heads, max_query_len=d["max_q"],
+                                           workspace=d["ws"])
+        return w, a
+
+    def timed(d):
+        w, a = step_fns(d)
+        for _ in range(max(1, args.warmup)):
+            w()
+            a()
+        torch.cuda.synchronize()
+        K = args.steps
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        for e0, e1, e2 in ev:
+            e0.record()
+            w()
+            e1.record()
+            a()
+            e2.record()
+        torch.cuda.synchronize()
+        wr = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+        at = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+        return wr, at
+
+    res = {}
+    for cached in (True, False):
+        d = build(cached)
+        torch.cuda.synchronize()
+        wr, at = timed(d)
+        res[cached] = (d, wr, at)
+        log(f"{'cached' if cached else 'plain '}: {d['written']} rows written ({d['hit']} cached), "
+            f"write {wr * 1e3:.1f} us, prefill {at * 1e3:.1f} us")
+    d, wr, at = res[True]
+    _, pwr, pat = res[False]
+    prompt_tokens = int(d["ctx_np"].sum())
+    C, L = d["chunks"], d["ctx_np"]
+    visible = int(sum(int(((L[i] - C[i] + 1) + L[i]) * C[i] // 2) for i in range(len(C))))
+    flops = visible * 4 * 128 * wl.num_heads
+    tflops = flops / (at * 1e-3) / 1e12
+    peak = 2500.0
+    step_ms = wr + at
+    result = {
+        "metric": "prefix-cached prompt admission: prompt tokens/s (write + chunked prefill) at 1 GPU",
+        "value": round(prompt_tokens / (step_ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": desc, "name": name, "requests": len(reqs), "num_heads": wl.num_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_size": 128, "block_size": 16,
+                   "prompt_tokens": prompt_tokens, "cached_tokens": d["hit"], "written_tokens": d["written"],
+                   "step": "reshape_and_cache (uncached rows) + paged_attn_prefill (uncached queries)",
+                   "parallelism": "single GPU"},
+        "without_prefix_cache": {"tokens_per_s": round(prompt_tokens / ((pwr + pat) * 1e-3), 1),
+                                 "write_us": round(pwr * 1e3, 2), "prefill_us": round(pat * 1e3, 2)},
+        "speedup": round((pwr + pat) / step_ms, 3),
+        "write_us": round(wr * 1e3, 2), "prefill_us": round(at * 1e3, 2),
+        "host_us_per_request": {"add_cached": round(host[True], 2), "add": round(host[False], 2)},
+        "roofline": {"bound": "mfma", "kernel": "paged_attn_prefill: prefill_kernel", "achieved": round(tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +480,8 @@ def main() -> int:
         return prefill_bench(args, args.workload)
     if args.workload.startswith("swap_"):
         return swap_bench(args, args.workload)
+    if args.workload.startswith("prefix_"):
+        return prefix_bench(args, args.workload)
     wl = synth.make_workload(args.workload)
     log(f"workload {wl.spec.name}: {wl.spec.description}")
     t0 = time.perf_counter()

@@ -324,3 +324,123 @@ def build_prefill(wl, device="cuda", *, garbage: str = "nan", garbage_seed: int 
     if run:
         pre.run()
     return pre
+
+
+# --------------------------------------------------------------------------
+# prefix caching end to end
+# --------------------------------------------------------------------------
+
+@dataclass
+class PrefixPhase:
+    """One prefill call of a prefix-cache run: sequence ``seqs[i]`` (a request
+    id) has ``context_lens[i]`` tokens and its queries are at positions
+    ``first_pos[i]`` .. ``context_lens[i] - 1`` (output rows query_start[i] ..)."""
+    seqs: list
+    context_lens: np.ndarray
+    first_pos: np.ndarray
+    query_start: np.ndarray
+    out: object
+
+
+@dataclass
+class PrefixRun:
+    phases: list
+    cached: dict        # request -> tokens add_cached reported as cached
+    written: int        # rows written by reshape_and_cache over the run
+    min_free_list: int  # shortest free list seen after any allocation
+    evictable_seen: list
+
+
+def run_prefix_cache(wl, *, cached: bool = True, first_pos=None, device="cuda") -> PrefixRun:
+    """Serve ``wl`` (synth.PrefixCacheWorkload) through the library: block
+    manager (add_cached / append_token, or add / append_slot when ``cached`` is
+    False), reshape_and_cache[_fp8] of the rows that are not cached yet, and
+    one paged_attn_prefill call per phase (phase 2 mixes the new prompts'
+    chunks with one decode token per surviving phase-1 request).  A prompt
+    found whole in the cache recomputes its last token (a chunk of 1).
+    ``first_pos`` (request -> first query position, per phase) forces the
+    chunks, so a run without caching can evaluate the same queries."""
+    import torch
+
+    fp8 = wl.kv_dtype == "fp8e4m3"
+    tdt = torch_dtype(wl.dtype)
+    k_cache, v_cache = pkv.allocate_cache(wl.pool_blocks, wl.num_kv_heads, torch.uint8 if fp8 else tdt, device)
+    bits = torch.uint8 if fp8 else torch.int16
+    k_cache.view(bits).fill_(255 if fp8 else -1)  # NaN everywhere nothing was written
+    v_cache.view(bits).fill_(255 if fp8 else -1)
+    bm = pkv.BlockManager(wl.pool_blocks, BS, wl.free_order)
+    got_cached, written = {}, 0
+    phases, evictable_seen, min_free = [], [], wl.pool_blocks
+    lens = {}
+
+    def write(slots, k, v):
+        nonlocal written
+        if len(slots) == 0:
+            return
+        write_rows(wl, to_device(k, wl.dtype, device), to_device(v, wl.dtype, device), k_cache, v_cache,
+                   torch.from_numpy(np.asarray(slots, dtype=np.int32)).to(device))
+        written += len(slots)
+
+    def add_prompt(r, phase):
+        ids, k, v = wl.prompt(r)
+        L = ids.shape[0]
+        if cached:
+            slots, c = bm.add_cached(r, ids)
+        else:
+            slots, c = bm.add(r, L), 0
+        got_cached[r] = c
+        write(slots[c:], k[c:], v[c:])
+        lens[r] = L
+        track()
+        fp = min(c, L - 1) if first_pos is None else first_pos[phase][r]
+        return fp
+
+    def track():
+        nonlocal min_free
+        min_free = min(min_free, bm.free_list().shape[0])
+        evictable_seen.append(bm.num_evictable())
+
+    def prefill(seqs, fps, phase):
+        S = len(seqs)
+        ctx = np.array([lens[r] for r in seqs], dtype=np.int64)
+        fps = np.asarray(fps, dtype=np.int64)
+        chunks = ctx - fps
+        qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int64)
+        q = np.concatenate([wl.q_rows(r)[fp:L] for r, fp, L in zip(seqs, fps, ctx)])
+        mb = max(bm.num_seq_blocks(r) for r in seqs)
+        tables = bm.block_table(seqs, mb)
+        out = torch.empty((int(qs[-1]), wl.num_heads, 128), dtype=tdt, device=device)
+        scales = dict(k_scale=wl.k_scale, v_scale=wl.v_scale) if fp8 else {}
+        pkv.paged_attn_prefill(out, to_device(q, wl.dtype, device), k_cache, v_cache,
+                               torch.from_numpy(tables).to(device),
+                               torch.from_numpy(ctx.astype(np.int32)).to(device),
+                               torch.from_numpy(qs.astype(np.int32)).to(device), wl.scale, wl.num_kv_heads,
+                               max_query_len=int(chunks.max()), **scales)
+        phases.append(PrefixPhase(seqs=list(seqs), context_lens=ctx, first_pos=fps, query_start=qs, out=out))
+
+    # phase 1: prompts
+    seqs1 = list(range(wl.phase1))
+    fps1 = [add_prompt(r, 0) for r in seqs1]
+    prefill(seqs1, fps1, 0)
+    torch.cuda.synchronize()
+    for r in wl.freed.tolist():
+        bm.free_seq(r)
+    evictable_seen.append(bm.num_evictable())
+    # phase 2: a decode token for each survivor, then the new prompts
+    survivors = [r for r in seqs1 if r not in set(wl.freed.tolist())]
+    fps2 = []
+    for r in survivors:
+        tid, k, v = wl.decode_token(r)
+        slot, cow = bm.append_token(r, tid) if cached else bm.append_slot(r)
+        assert cow is None  # no request shares a partial block here
+        write([slot], k[None], v[None])
+        track()
+        fps2.append(lens[r] if first_pos is None else first_pos[1][r])
+        lens[r] += 1
+    news = list(range(wl.phase1, wl.num_requests))
+    for r in news:
+        fps2.append(add_prompt(r, 1))
+    prefill(survivors + news, fps2, 1)
+    torch.cuda.synchronize()
+    return PrefixRun(phases=phases, cached=got_cached, written=written, min_free_list=min_free,
+                     evictable_seen=evictable_seen)

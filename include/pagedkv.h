@@ -167,8 +167,9 @@ int32_t paged_attn_decode_partition_tokens(int32_t num_seqs, int32_t num_heads,
  * arrive; the slot encoding block * 16 + offset is this library's convention).
  *
  *   k, v          [num_tokens, num_kv_heads, 128] cache dtype, contiguous
- *   slot_mapping  int32 [num_tokens]; negative = padding, skipped; slots must be
- *                 unique (two tokens writing one slot race)
+ *   slot_mapping  int32 [num_tokens]; negative = padding, skipped (so is a slot
+ *                 >= num_blocks * 16); slots must be unique (two tokens writing
+ *                 one slot race)
  * Bit-exact copy of the input bits.  num_tokens == 0 is a no-op.
  * ------------------------------------------------------------------------- */
 pkv_status reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -494,3 +494,154 @@ PREFILL_CONFIGS = {
 def make_prefill(name: str) -> PrefillWorkload:
     cfg = dict(PREFILL_CONFIGS[name])
     return make_prefill_workload(cfg.pop("seed"), name=name, **cfg)
+
+
+# --------------------------------------------------------------------------
+# prefix caching: requests that share system prompts, in two phases
+# --------------------------------------------------------------------------
+
+@dataclass
+class PrefixCacheWorkload:
+    """Requests built as (a prefix of one of a few system prompts) + (their own
+    tokens), served in two phases: phase 1 adds ``phase1`` requests; then the
+    requests in ``freed`` finish; phase 2 adds the remaining requests while
+    every phase-1 survivor decodes one token.  A phase-2 request with
+    ``req_parent[r] >= 0`` is the next turn of a finished request: its prompt
+    is that request's prompt followed by its own tokens.  Token ids and K/V
+    rows of a shared prefix are the same in every request that holds it (K/V of
+    a token is a function of its whole prefix, and these prefixes are equal).
+
+    Streams: main ``default_rng(seed)`` (prompt lengths, request shapes, freed
+    set, pool permutation); system prompt j: ids ``default_rng([seed, 4, j])``,
+    K then V ``default_rng([seed, 5, j])``; request r: ids then K then V
+    ``default_rng([seed, 6, r])``; the decode token of r: id then K then V
+    ``default_rng([seed, 7, r])``; q rows of r's positions 0 .. L_r
+    ``default_rng([seed, 8, r])``."""
+
+    seed: int
+    num_heads: int
+    num_kv_heads: int
+    dtype: str
+    sys_lens: np.ndarray    # int64 [P]
+    req_sys: np.ndarray     # int64 [R]: which system prompt
+    req_keep: np.ndarray    # int64 [R]: how many of its tokens the request starts with
+    req_own: np.ndarray     # int64 [R]: own tokens after them (>= 1)
+    req_parent: np.ndarray  # int64 [R]: the finished request this one continues, or -1
+    phase1: int
+    freed: np.ndarray       # int64: phase-1 requests that finish before phase 2
+    free_order: np.ndarray  # int32 [pool]
+    kv_dtype: Optional[str] = None
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    vocab: int = 32000
+
+    @property
+    def num_requests(self) -> int:
+        return int(self.req_sys.shape[0])
+
+    @property
+    def pool_blocks(self) -> int:
+        return int(self.free_order.shape[0])
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(HEAD_SIZE)
+
+    def prompt_len(self, r: int) -> int:
+        p = int(self.req_parent[r])
+        base = self.prompt_len(p) if p >= 0 else int(self.req_keep[r])
+        return base + int(self.req_own[r])
+
+    def _sys(self, j: int):
+        n = int(self.sys_lens[j])
+        ids = np.random.default_rng([self.seed, 4, j]).integers(0, self.vocab, n)
+        rng = np.random.default_rng([self.seed, 5, j])
+        k = rng.standard_normal((n, self.num_kv_heads, HEAD_SIZE), dtype=np.float32)
+        v = rng.standard_normal((n, self.num_kv_heads, HEAD_SIZE), dtype=np.float32)
+        return ids, k, v
+
+    def prompt(self, r: int):
+        """(token ids int64 [L], K, V storage dtype [L, Hkv, D]) of request r's prompt."""
+        own = int(self.req_own[r])
+        rng = np.random.default_rng([self.seed, 6, r])
+        oid = rng.integers(0, self.vocab, own)
+        ok = _to_storage(rng.standard_normal((own, self.num_kv_heads, HEAD_SIZE), dtype=np.float32), self.dtype)
+        ov = _to_storage(rng.standard_normal((own, self.num_kv_heads, HEAD_SIZE), dtype=np.float32), self.dtype)
+        p = int(self.req_parent[r])
+        if p >= 0:
+            ids, k, v = self.prompt(p)
+        else:
+            keep = int(self.req_keep[r])
+            ids, k, v = self._sys(int(self.req_sys[r]))
+            ids, k, v = ids[:keep], _to_storage(k[:keep], self.dtype), _to_storage(v[:keep], self.dtype)
+        return np.concatenate([ids, oid]), np.concatenate([k, ok]), np.concatenate([v, ov])
+
+    def decode_token(self, r: int):
+        """(id, K [Hkv, D], V [Hkv, D]) of the token request r decodes in phase 2."""
+        rng = np.random.default_rng([self.seed, 7, r])
+        tid = int(rng.integers(0, self.vocab))
+        k = rng.standard_normal((self.num_kv_heads, HEAD_SIZE), dtype=np.float32)
+        v = rng.standard_normal((self.num_kv_heads, HEAD_SIZE), dtype=np.float32)
+        return tid, _to_storage(k, self.dtype), _to_storage(v, self.dtype)
+
+    def q_rows(self, r: int):
+        """q of request r at positions 0 .. prompt_len(r) (the last: its decode token)."""
+        rng = np.random.default_rng([self.seed, 8, r])
+        q = rng.standard_normal((self.prompt_len(r) + 1, self.num_heads, HEAD_SIZE), dtype=np.float32)
+        return _to_storage(q, self.dtype)
+
+
+def make_prefix_cache_workload(seed: int, *, num_heads: int = 8, num_kv_heads: int = 2, dtype: str = "fp16",
+                               sys_lens=(40, 150, 300), phase1: int = 12, phase2: int = 12,
+                               own: Tuple[int, int] = (1, 120), kv_dtype: Optional[str] = None,
+                               k_scale: float = 1.0, v_scale: float = 1.0,
+                               pool_blocks: Optional[int] = None, keep_prob: float = 0.7) -> PrefixCacheWorkload:
+    """Each request takes a system prompt (uniformly), keeps all of it with
+    probability ``keep_prob`` (else a uniform cut), and adds U[own] own tokens; half the
+    phase-1 requests finish, and each phase-2 request continues one of them
+    with probability 0.3.  The pool is the largest number of blocks the live
+    requests hold without any sharing, so the run always fits and the freed,
+    registered blocks must be evicted once the free list runs out.  Given
+    ``pool_blocks``, the pool has that many blocks instead (everything else is
+    drawn the same)."""
+    rng = np.random.default_rng(seed)
+    sys_lens = np.asarray(sys_lens, dtype=np.int64)
+    R = phase1 + phase2
+    req_sys = rng.integers(0, len(sys_lens), R)
+    full = rng.random(R) < keep_prob
+    cut = np.array([rng.integers(0, sys_lens[j] + 1) for j in req_sys], dtype=np.int64)
+    req_keep = np.where(full, sys_lens[req_sys], cut).astype(np.int64)
+    req_own = rng.integers(own[0], own[1], R, endpoint=True).astype(np.int64)
+    freed = np.sort(rng.choice(phase1, phase1 // 2, replace=False)).astype(np.int64)
+    follow = rng.random(R) < 0.3
+    pick = rng.integers(0, max(1, freed.shape[0]), R)
+    req_parent = np.full(R, -1, dtype=np.int64)
+    if freed.shape[0]:
+        req_parent[phase1:] = np.where(follow[phase1:], freed[pick[phase1:]], -1)
+    blocks = lambda n: -(-int(n) // BLOCK_SIZE)  # noqa: E731
+    L = np.array([req_keep[r] + req_own[r] if req_parent[r] < 0 else req_keep[req_parent[r]]
+                  + req_own[req_parent[r]] + req_own[r] for r in range(R)], dtype=np.int64)
+    peak1 = sum(blocks(L[r]) for r in range(phase1))
+    peak2 = (sum(blocks(L[r] + 1) for r in range(phase1) if r not in set(freed.tolist()))
+             + sum(blocks(L[r]) for r in range(phase1, R)))
+    pool = max(peak1, peak2) if pool_blocks is None else int(pool_blocks)
+    free_order = rng.permutation(pool).astype(np.int32)
+    return PrefixCacheWorkload(seed=seed, num_heads=num_heads, num_kv_heads=num_kv_heads, dtype=dtype,
+                               sys_lens=sys_lens, req_sys=req_sys, req_keep=req_keep, req_own=req_own,
+                               req_parent=req_parent, phase1=phase1, freed=freed, free_order=free_order, kv_dtype=kv_dtype,
+                               k_scale=k_scale, v_scale=v_scale)
+
+
+PREFIX_CONFIGS = {
+    "prefix_llama13b": dict(seed=31, num_heads=40, num_kv_heads=40, dtype="fp16", sys_lens=(1024,), phase1=1,
+                            phase2=64, own=(128, 512), keep_prob=1.0,
+                            description="prefix-cached prompt admission, LLaMA-13B-shaped: 40 MHA heads, fp16; "
+                                        "64 new prompts = one shared 1024-token system prompt (already served "
+                                        "once) + U[128,512] own tokens"),
+}
+
+
+def make_prefix(name: str):
+    cfg = dict(PREFIX_CONFIGS[name])
+    desc = cfg.pop("description")
+    return make_prefix_cache_workload(cfg.pop("seed"), **cfg), desc

@@ -234,3 +234,60 @@ def test_fork_then_generate_shares_and_registers():
         bm.append_token(1, 300 + t)
     _, c = bm.add_cached(2, list(range(20)) + [98] + list(range(300, 311)))
     assert c == 32 and bm.blocks[2][1] == bm.blocks[1][1]
+
+
+def _serve(wl):
+    """The host side of the two-phase request mix the GPU test serves, on the
+    oracle block manager with the token-prefix stand-in cache."""
+    bm = BlockManager(wl.pool_blocks, BS, wl.free_order)
+    cache, toks = {}, {}
+    st = dict(hits=0, revived=0, min_free=wl.pool_blocks, peak_used=0)
+
+    def add(r):
+        ids = wl.prompt(r)[0].tolist()
+        ev = bm.num_evictable()
+        slots, c = bm.add_cached(r, ids)
+        st["hits"] += c
+        st["revived"] += ev - bm.num_evictable() > 0
+        for t in range(c, len(ids)):
+            cache[slots[t]] = tuple(ids[:t + 1])
+        toks[r] = ids
+        st["min_free"] = min(st["min_free"], len(bm.free))
+        st["peak_used"] = max(st["peak_used"], bm.num_used())
+
+    for r in range(wl.phase1):
+        add(r)
+    for r in wl.freed.tolist():
+        bm.free_seq(r)
+        del toks[r]
+    assert bm.num_evictable() > 0
+    for r in list(toks):
+        tid = wl.decode_token(r)[0]
+        slot, cow = bm.append_token(r, tid)
+        assert cow is None
+        toks[r].append(tid)
+        cache[slot] = tuple(toks[r])
+        st["peak_used"] = max(st["peak_used"], bm.num_used())
+    for r in range(wl.phase1, wl.num_requests):
+        add(r)
+    _check_pool(bm)
+    for r, ids in toks.items():
+        for t in range(len(ids)):
+            assert cache[bm.blocks[r][t // BS] * BS + t % BS] == tuple(ids[:t + 1])
+    return st
+
+
+@pytest.mark.parametrize("seed", [901, 906, 907, 908, 918])  # the GPU test's mixes
+def test_prefix_workload_reuses_revives_and_evicts(seed):
+    """Run on the pool without sharing, the mix reuses and revives blocks; run
+    again on a pool of just its peak of blocks in use (eviction takes only
+    blocks no live request holds, so that peak does not change), it fits,
+    exhausts the free list and so evicts, and every request still reads its
+    own prefixes."""
+    import synth
+    loose = _serve(synth.make_prefix_cache_workload(seed))
+    assert loose["min_free"] > 0  # nothing evicted: every drop of the evictable count is a revival
+    assert loose["hits"] > 0 and loose["revived"] > 0
+    tight = _serve(synth.make_prefix_cache_workload(seed, pool_blocks=loose["peak_used"]))
+    assert tight["min_free"] == 0 and tight["peak_used"] == loose["peak_used"]
+    assert 0 < tight["hits"] <= loose["hits"]
