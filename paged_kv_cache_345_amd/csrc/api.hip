@@ -422,7 +422,7 @@ pkv_status prefill_layout(int32_t num_seqs, int32_t num_heads, int32_t max_block
   P.group = num_heads / cache->num_kv_heads;
   P.hpt = P.group < 16 ? P.group : 16;
   P.ppt = 16 / P.hpt;
-  const int32_t per_wg = pkv::kWavesPerGroup * P.ppt;
+  const int32_t per_wg = pkv::kWavesPerGroup * pkv::kPrefillTiles * P.ppt;
   P.q_blocks = max_query_len > 0 ? (max_query_len + per_wg - 1) / per_wg : 0;
   P.units = cache->num_kv_heads * ((P.group + 15) / 16);
   // Segment length.  Automatic: the whole key range (the smallest power of

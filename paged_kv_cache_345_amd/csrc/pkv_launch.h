@@ -51,15 +51,18 @@ struct DecodeArgs {
 
 // Chunked prefill: chunk query j of sequence s (output row query_start[s] + j)
 // sits at position context_lens[s] - C_s + j and attends to cache tokens
-// 0 .. that position.  A work-group takes 4 x 16 rows (query position, head) of
-// one KV head: wave w the positions [4 ppt qb + w ppt, + ppt) for heads_per_tile
-// heads each; all 4 waves stream the same blocks.
+// 0 .. that position.  A work-group takes kPrefillTiles x 4 tiles of 16 rows
+// (query position, head) of one KV head: tile i of the work-group covers the
+// positions [8 ppt qb + i ppt, + ppt) for heads_per_tile heads each; wave w
+// holds tiles kPrefillTiles w .. + kPrefillTiles - 1, and the work-group
+// stages the blocks it streams in LDS once for all its waves.
+constexpr int kPrefillTiles = 2;  // 16-row tiles per wave
 struct PrefillArgs {
   DecodeArgs d;                // out, q and the partials are per query token
   const int32_t* query_start;  // [num_seqs + 1]
   int heads_per_tile;          // hpt = min(group, 16)
-  int pos_per_wave;            // ppt = 16 / hpt
-  int q_blocks;                // ceil(max_query_len / (4 ppt))
+  int pos_per_wave;            // ppt = 16 / hpt: positions per tile
+  int q_blocks;                // ceil(max_query_len / (4 kPrefillTiles ppt))
   int num_query_tokens;
 };
 

@@ -10,30 +10,78 @@
 namespace pkv {
 
 // ---------------------------------------------------------------------------
-// Chunked prefill: 4 waves x 16 (query position, head) rows of one KV head per
-// work-group, on the matrix cores.  Each wave streams the work-group's whole
-// segment of blocks for its own 16 rows (the 4 waves read the same pages at
-// about the same time, so the repeats hit the compute unit's cache), masks
-// every key beyond its row's position, and writes its rows itself.
+// Chunked prefill on the matrix cores.  A work-group takes 8 tiles of 16
+// (query position, head) rows of one KV head, two tiles per wave, and streams
+// the blocks of its segment in steps of kStageBlocks blocks.  Each step's K
+// and V pages go straight from the cache into LDS (buffer loads with the LDS
+// destination bit), kStageBufs - 1 steps ahead of the one being computed, and
+// every wave reads its fragments from there for both of its tiles.  Per step
+// and tile: S = K Q^T (16x16x32 products), one online-softmax update over the
+// step's keys (the causal mask by row position is evaluated only in steps
+// that reach past some row's position), then O += P V (16x16x16 products).
+// A block wholly past every position of a wave is skipped by that wave.  Each
+// wave writes its own rows.
+//
+// The step loads are issued from inline assembly: with the compiler's own LDS
+// loads, it waits for every load in flight before each LDS read and each
+// barrier, which leaves no load ahead of the step being computed (measured on
+// MI355X: staging one step ahead through registers instead gave 1.6x longer
+// calls on both prefill batches).  The kernel therefore keeps the vector-memory
+// counter itself: no other vector memory access happens in the step loop
+// (block ids are scalar loads, q is taken before the loop), each wave waits
+// for its own loads of the next step, and the work-group barrier follows.
+// M0, which the loads take their LDS address from, has no other use in this
+// kernel's code.
 // ---------------------------------------------------------------------------
+
+constexpr int kStageBlocks = 2;  // blocks per LDS step
+constexpr int kStageBufs = 4;    // LDS step buffers: up to kStageBufs - 1 steps in flight
 
 // Blocks that the work-group holding chunk query qi streams: up to the block
 // of its last query's position.  Shared by the prefill kernel and its reduce.
 __device__ inline int prefill_wg_blocks(const PrefillArgs& pa, int L, int C, int qi) {
-  const int per_wg = kWavesPerGroup * pa.pos_per_wave;
+  const int per_wg = kWavesPerGroup * kPrefillTiles * pa.pos_per_wave;
   const int last_q = min(C, (qi / per_wg + 1) * per_wg) - 1;
   return (L - C + last_q) / kBlockSize + 1;
 }
 
+// Fragment reads from a page copy in LDS, in the page formats' register layout
+// (lane l's 16 bytes of wave load i sit at byte 1024 i + 16 l of the page).
+template <class PF>
+struct LdsPage;
+template <>
+struct LdsPage<Page16> {
+  __device__ static inline void k(const char* pg, int lane, uint4 (&kv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kv[i] = *reinterpret_cast<const uint4*>(pg + 1024 * i + 16 * lane);
+  }
+  __device__ static inline void v(const char* pg, int lane, uint4 (&vv)[4]) { k(pg, lane, vv); }
+};
+template <class DT>
+struct LdsPage<PageFp8<DT>> {
+  __device__ static inline void k(const char* pg, int lane, uint4 (&kv)[4]) {
+    const uint4 w0 = *reinterpret_cast<const uint4*>(pg + 16 * lane);
+    const uint4 w1 = *reinterpret_cast<const uint4*>(pg + 1024 + 16 * lane);
+    PageFp8<DT>::widen(w0, kv[0], kv[1]);
+    PageFp8<DT>::widen(w1, kv[2], kv[3]);
+  }
+  __device__ static inline void v(const char* pg, int lane, uint4 (&vv)[4]) { k(pg, lane, vv); }
+};
+
 template <class DT, class PF>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs pa) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pa) {
+  constexpr int kPage = PF::kPageBytes;
+  constexpr int kPieces = kPage / 1024;                          // 1 KiB wave loads per page
+  constexpr int kLoads = 2 * kStageBlocks * kPieces / kWavesPerGroup;  // wave loads per wave per step
+  __shared__ __attribute__((aligned(16))) char lds[kStageBufs][2][kStageBlocks][kPage];  // [buffer][K, V][block]
+
   const DecodeArgs& a = pa.d;
   // item (unit, sequence, query block, segment), segment fastest; XCD-aware
   // chunks as in decode's direct mode
   const int64_t total = static_cast<int64_t>(a.units) * a.num_seqs * pa.q_blocks * a.parts_max;
   const int64_t per_xcd = (total + kNumXcd - 1) / kNumXcd;
   const int64_t lam = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
-  if (lam >= total) return;
+  if (lam >= total) return;  // uniform over the work-group
   const int g = static_cast<int>(lam % a.parts_max);
   int64_t rest = lam / a.parts_max;
   const int qb = static_cast<int>(rest % pa.q_blocks);
@@ -49,11 +97,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs pa) {
   const int q0 = pa.query_start[s];
   const int C = min(max(pa.query_start[s + 1] - q0, 0), L);
   const int ppt = pa.pos_per_wave;
-  const int wg_q0 = qb * kWavesPerGroup * ppt;
+  const int wg_q0 = qb * kWavesPerGroup * kPrefillTiles * ppt;
   if (wg_q0 >= C) return;  // uniform over the work-group
   const int nblk = prefill_wg_blocks(pa, L, C, wg_q0);
   const int nseg = (nblk + a.blocks_per_part - 1) / a.blocks_per_part;
-  if (g >= nseg) return;
+  if (g >= nseg) return;  // uniform over the work-group
   const int j0 = g * a.blocks_per_part;
   const int nb = min(a.blocks_per_part, nblk - j0);
 
@@ -62,91 +110,271 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs pa) {
   const int grp = lane >> 4;
   const int col = lane & 15;
   const int hpt = pa.heads_per_tile;
-  // tile row r of this wave: position index r / hpt, head index r % hpt
-  auto row_query = [&](int r) { return wg_q0 + wave * ppt + r / hpt; };
-  auto row_valid = [&](int r) { return r / hpt < ppt && r % hpt < nh && row_query(r) < C; };
-  const int pos_col = row_valid(col) ? L - C + row_query(col) : -1;  // -1: every key masked
-  if (__ballot(pos_col >= 0) == 0) return;  // no row of this wave is a query (no barrier follows)
-
-  float m = kInitMax;
-  float z = 0.f;
-  float4_t O[8];
+  // row r of tile T of this wave: position index r / hpt, head index r % hpt
+  auto row_query = [&](int T, int r) { return wg_q0 + (kPrefillTiles * wave + T) * ppt + r / hpt; };
+  auto row_valid = [&](int T, int r) { return r / hpt < ppt && r % hpt < nh && row_query(T, r) < C; };
+  int pos[kPrefillTiles];  // position of row col of each tile; -1: no query (every key masked)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) O[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 qf[4];
-  if (pos_col >= 0) {
-    const uint4* qrow = reinterpret_cast<const uint4*>(
-        a.q + (static_cast<int64_t>(q0 + row_query(col)) * a.num_heads + h0 + col % hpt) * kHeadSize);
+  for (int T = 0; T < kPrefillTiles; ++T) pos[T] = row_valid(T, col) ? L - C + row_query(T, col) : -1;
+  // the wave's position range over its valid rows (wave-uniform)
+  int hi_pos = max(pos[0], pos[kPrefillTiles - 1]);
+  int lo_pos = pos[0] >= 0 ? pos[0] : 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qf[i] = qrow[4 * i + grp];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qf[i] = make_uint4(0, 0, 0, 0);
+  for (int d = 32; d > 0; d >>= 1) {
+    hi_pos = max(hi_pos, __shfl_xor(hi_pos, d, kWave));
+    lo_pos = min(lo_pos, __shfl_xor(lo_pos, d, kWave));
   }
 
-  auto process = [&]<bool kTail>(uint4 (&kv)[4], uint4 (&vv)[4], int j) __attribute__((always_inline)) {
-    const int nvalid = kTail ? min(kBlockSize, L - j * kBlockSize) : kBlockSize;
-    float4_t S = {0.f, 0.f, 0.f, 0.f};
+  float m[kPrefillTiles], z[kPrefillTiles];
+  float4_t O[kPrefillTiles][8];
+  uint4 qf[kPrefillTiles][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S = DT::mfma_qk(kv[i], qf[i], S);
-    float x[4];
-    const int t0 = j * kBlockSize + 4 * grp;
+  for (int T = 0; T < kPrefillTiles; ++T) {
+    m[T] = kInitMax;
+    z[T] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = t0 + r <= pos_col ? S[r] * a.scale_log2e : kMaskedLogit;
-
-    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = cross_row_max(bm);
-    const float m_new = fmaxf(m, bm);
-    const float alpha = exp2_fast(m - m_new);
-    m = m_new;
-    float pr[4];
+    for (int j = 0; j < 8; ++j) O[T][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    if (pos[T] >= 0) {
+      const uint4* qrow = reinterpret_cast<const uint4*>(
+          a.q + (static_cast<int64_t>(q0 + row_query(T, col)) * a.num_heads + h0 + col % hpt) * kHeadSize);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = DT::round(exp2_fast(x[r] - m_new));
-    z = z * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    float ar[4];
+      for (int i = 0; i < 4; ++i) qf[T][i] = qrow[4 * i + grp];
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ar[r] = lane_from(alpha, 4 * grp + r);
-#pragma unroll
-    for (int jd = 0; jd < 8; ++jd) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) O[jd][r] *= ar[r];
+      for (int i = 0; i < 4; ++i) qf[T][i] = make_uint4(0, 0, 0, 0);
     }
-    uint2 pa2;
-    pa2.x = DT::pack2(pr[0], pr[1]);
-    pa2.y = DT::pack2(pr[2], pr[3]);
-    if (kTail && nvalid < kBlockSize) mask_v(vv, grp, nvalid);  // stale slots past the context
+  }
+  // Take the q loads' results here: the step loads below go to LDS behind the
+  // compiler's back, and a wait for q left inside the loop would also wait for
+  // every step load in flight.
 #pragma unroll
-    for (int jd = 0; jd < 8; ++jd) {
-      const uint4& f = vv[jd >> 1];
-      const uint2 b = (jd & 1) ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y);
-      O[jd] = DT::mfma_pv(pa2, b, O[jd]);
+  for (int T = 0; T < kPrefillTiles; ++T)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      asm volatile("" : "+v"(qf[T][i].x), "+v"(qf[T][i].y), "+v"(qf[T][i].z), "+v"(qf[T][i].w));
+
+  // step loads, straight from the cache into LDS: wave w makes the step's
+  // 1 KiB pieces kLoads w .. kLoads w + kLoads - 1 (piece p: page p / kPieces,
+  // K pages first, then V; lane l's 16 bytes land at byte 16 l of the piece)
+  const int32_t* brow = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq + j0;
+  const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kPage;
+  const int64_t head_off = static_cast<int64_t>(kvh) * kPage;
+  const char* kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache);
+  auto issue = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int p = kLoads * wave + i;
+      const int pg = p / kPieces;
+      const int b = pg % kStageBlocks;
+      const int jj = st * kStageBlocks + b;
+      // block id by a scalar load (the asm memory clobbers below keep the
+      // compiler from proving the table unchanged, so it would use a vector
+      // load and a wait that also drains the step loads in flight)
+      int bid;
+      asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                   : "=s"(bid) : "s"(brow + min(jj, nb - 1)) : "memory");
+      const bool bad = jj >= nb || static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks);
+      const char* page = (pg < kStageBlocks ? kc : vc) + (bad ? 0 : bid) * page_stride + head_off;
+      const __amdgpu_buffer_rsrc_t r = range_rsrc(page, bad ? 0 : kPage);  // a bad id reads zeros
+      // LDS byte address of the piece (the low 32 bits of its generic address)
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>(&lds[st % kStageBufs][pg / kStageBlocks][b][1024 * (p % kPieces)])));
+      const uint32_t off = 1024u * (p % kPieces) + 16u * lane;
+      // K: non-temporal, V: default policy, as in the decode page loads.  The
+      // load goes to LDS (lane l's 16 bytes at dst + 16 l) and is counted by the
+      // vector-memory counter, which wait_steps below checks.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is written here and read by nothing else
+      if (pg < kStageBlocks)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                     :: "s"(dst), "v"(off), "s"(r) : "memory", "m0");
+      else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(dst), "v"(off), "s"(r) : "memory", "m0");
+#pragma clang diagnostic pop
     }
   };
-  stream_blocks<PF>(a, s, kvh, j0, nb, lane, process);
+  // Work-group barrier between steps.  Before it each wave has waited for its
+  // own loads of the step about to be read (wait_steps) and for its own LDS
+  // reads (their data is consumed before the barrier, and the buffer they read
+  // is refilled after it).  __syncthreads() would also drain every load still
+  // in flight for the later steps.
+  auto step_barrier = []() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // wait until at most n steps' loads of this wave are still in flight
+  auto wait_steps = [&](int n) __attribute__((always_inline)) {
+    if (n >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * kLoads) : "memory");
+    else if (n == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kLoads) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
 
-  // O[jd][r]: row 4grp + r, dim 16 jd + col; lane c (< 16) holds row c's max and sum
-  const float Zc = cross_row_sum(z);
+  const float sc = a.scale_log2e;
+  const uint32_t ones = DT::pack2(1.f, 1.f);
+  // One step over blocks jstep .. jstep + n - 1 (n >= 1, wave-uniform).  kFast:
+  // n == kStageBlocks and every valid row of the wave sees every key, so no
+  // mask is evaluated (rows without a query compute garbage they never write).
+  auto step = [&]<bool kFast>(int buf, int jstep, int n) __attribute__((always_inline)) {
+    float4_t S[kPrefillTiles][kStageBlocks];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int tr = 4 * grp + r;
-    const float Zr = lane_from(Zc, tr);
-    const float mr = lane_from(m, tr);
-    if (!row_valid(tr)) continue;
-    const int64_t orow = static_cast<int64_t>(q0 + row_query(tr)) * a.num_heads + h0 + tr % hpt;
-    if (nseg == 1) {
-      uint16_t* dst = a.out + orow * kHeadSize + col;
-      const float inv = a.out_scale / Zr;
+    for (int b = 0; b < kStageBlocks; ++b) {
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd) dst[16 * jd] = DT::from_f32(O[jd][r] * inv);
-    } else {
-      const int64_t slot = orow * a.parts_max + g;
-      float* dst = a.ws_o + slot * kHeadSize + col;
+      for (int T = 0; T < kPrefillTiles; ++T) S[T][b] = float4_t{0.f, 0.f, 0.f, 0.f};
+      if (kFast || b < n) {
+        uint4 kv[4];
+        LdsPage<PF>::k(lds[buf][0][b], lane, kv);
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd) dst[16 * jd] = O[jd][r];
-      if (col == 0) {
-        a.ws_ml[2 * slot] = mr;
-        a.ws_ml[2 * slot + 1] = Zr;
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int T = 0; T < kPrefillTiles; ++T) S[T][b] = DT::mfma_qk(kv[i], qf[T][i], S[T][b]);
+        }
+      }
+    }
+
+    uint2 P[kPrefillTiles][kStageBlocks];
+#pragma unroll
+    for (int T = 0; T < kPrefillTiles; ++T) {
+      float m_new, alpha, zs = 0.f;
+      if (kFast) {
+        // row extreme of the raw scores (the max of S * sc is sc times the
+        // max of S for sc >= 0, the min otherwise)
+        float e = S[T][0][0];
+        if (sc >= 0.f) {
+#pragma unroll
+          for (int b = 0; b < kStageBlocks; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e = fmaxf(e, S[T][b][r]);
+          e = cross_row_max(e);
+        } else {
+#pragma unroll
+          for (int b = 0; b < kStageBlocks; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e = fminf(e, S[T][b][r]);
+          e = -cross_row_max(-e);
+        }
+        m_new = fmaxf(m[T], e * sc);
+        alpha = exp2_fast(m[T] - m_new);
+        const float neg = -m_new;
+#pragma unroll
+        for (int b = 0; b < kStageBlocks; ++b) {
+          P[T][b].x = DT::pack2(exp2_fast(fmaf(S[T][b][0], sc, neg)), exp2_fast(fmaf(S[T][b][1], sc, neg)));
+          P[T][b].y = DT::pack2(exp2_fast(fmaf(S[T][b][2], sc, neg)), exp2_fast(fmaf(S[T][b][3], sc, neg)));
+          zs = DT::dot2(P[T][b].x, ones, zs);
+          zs = DT::dot2(P[T][b].y, ones, zs);
+        }
+      } else {
+        float x[kStageBlocks][4];
+        float bm = kMaskedLogit;
+#pragma unroll
+        for (int b = 0; b < kStageBlocks; ++b) {
+          const int t0 = (jstep + b) * kBlockSize + 4 * grp;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[b][r] = b < n && t0 + r <= pos[T] ? S[T][b][r] * sc : kMaskedLogit;
+            bm = fmaxf(bm, x[b][r]);
+          }
+        }
+        bm = cross_row_max(bm);
+        m_new = fmaxf(m[T], bm);
+        alpha = exp2_fast(m[T] - m_new);
+#pragma unroll
+        for (int b = 0; b < kStageBlocks; ++b) {
+          P[T][b].x = DT::pack2(exp2_fast(x[b][0] - m_new), exp2_fast(x[b][1] - m_new));
+          P[T][b].y = DT::pack2(exp2_fast(x[b][2] - m_new), exp2_fast(x[b][3] - m_new));
+          zs = DT::dot2(P[T][b].x, ones, zs);
+          zs = DT::dot2(P[T][b].y, ones, zs);
+        }
+      }
+      m[T] = m_new;
+      z[T] = fmaf(z[T], alpha, zs);
+      // rescale O only when some row's running max moved (alpha == 1 exactly otherwise)
+      if (__ballot(alpha != 1.f) != 0) {
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = lane_from(alpha, 4 * grp + r);
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[T][jd][r] *= ar[r];
+        }
+      }
+    }
+
+    // O += P V
+#pragma unroll
+    for (int b = 0; b < kStageBlocks; ++b) {
+      if (!kFast && b >= n) continue;
+      uint4 vv[4];
+      LdsPage<PF>::v(lds[buf][1][b], lane, vv);
+      const int nvalid = L - (jstep + b) * kBlockSize;
+      if (!kFast && nvalid < kBlockSize) mask_v(vv, grp, nvalid);  // stale slots past the context
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) {
+        const uint4& f = vv[jd >> 1];
+        const uint2 bv = (jd & 1) ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y);
+#pragma unroll
+        for (int T = 0; T < kPrefillTiles; ++T) O[T][jd] = DT::mfma_pv(P[T][b], bv, O[T][jd]);
+      }
+    }
+  };
+
+  const int nsteps = (nb + kStageBlocks - 1) / kStageBlocks;
+  for (int st = 0; st < min(nsteps, kStageBufs - 1); ++st) issue(st);
+  wait_steps(min(nsteps, kStageBufs - 1) - 1);
+  step_barrier();
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st % kStageBufs;
+    // the buffer of step st + kStageBufs - 1 was last read in step st - 1, before the barrier that ended it
+    if (st + kStageBufs - 1 < nsteps) issue(st + kStageBufs - 1);
+
+    // live blocks of the step for this wave: a prefix (the step's blocks inside
+    // the segment, up to the wave's last position); the fast path takes steps
+    // whose 4 blocks are live and visible to every valid row of the wave
+    const int jstep = j0 + st * kStageBlocks;
+    const int nlive =
+        hi_pos < 0 ? 0 : max(0, min(min(kStageBlocks, nb - st * kStageBlocks), hi_pos / kBlockSize - jstep + 1));
+    const bool fast = nlive == kStageBlocks && (jstep + kStageBlocks) * kBlockSize - 1 <= lo_pos;
+    if (fast)
+      step.template operator()<true>(buf, jstep, kStageBlocks);
+    else if (nlive > 0)
+      step.template operator()<false>(buf, jstep, nlive);
+
+    if (st + 1 < nsteps) {
+      // step st + 1 landed; the steps after it that were issued may stay in flight
+      wait_steps(min(nsteps - 1, st + kStageBufs - 1) - (st + 1));
+      step_barrier();
+    }
+  }
+
+  // O[T][jd][r]: row 4grp + r, dim 16 jd + col; lane c (< 16) holds row c's max and sum
+#pragma unroll
+  for (int T = 0; T < kPrefillTiles; ++T) {
+    const float Zc = cross_row_sum(z[T]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = 4 * grp + r;
+      const float Zr = lane_from(Zc, tr);
+      const float mr = lane_from(m[T], tr);
+      if (!row_valid(T, tr)) continue;
+      const int64_t orow = static_cast<int64_t>(q0 + row_query(T, tr)) * a.num_heads + h0 + tr % hpt;
+      if (nseg == 1) {
+        uint16_t* dst = a.out + orow * kHeadSize + col;
+        const float inv = a.out_scale / Zr;
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) dst[16 * jd] = DT::from_f32(O[T][jd][r] * inv);
+      } else {
+        const int64_t slot = orow * a.parts_max + g;
+        float* dst = a.ws_o + slot * kHeadSize + col;
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) dst[16 * jd] = O[T][jd][r];
+        if (col == 0) {
+          a.ws_ml[2 * slot] = mr;
+          a.ws_ml[2 * slot + 1] = Zr;
+        }
       }
     }
   }
@@ -173,7 +401,7 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs pa) {
   const int qi = tq - q0;
   // no such query (a chunk longer than its context), or one past the grid
   // (a chunk longer than max_query_len): the prefill kernel wrote nothing for it
-  if (qi >= C || qi >= pa.q_blocks * kWavesPerGroup * pa.pos_per_wave) return;
+  if (qi >= C || qi >= pa.q_blocks * kWavesPerGroup * kPrefillTiles * pa.pos_per_wave) return;
   const int nblk = prefill_wg_blocks(pa, L, C, qi);
   const int n = (nblk + a.blocks_per_part - 1) / a.blocks_per_part;
   if (n <= 1) return;  // written directly by the prefill kernel
