@@ -431,7 +431,7 @@ pkv_status prefill_layout(int32_t num_seqs, int32_t num_heads, int32_t max_block
   // they do not; every wave of a prefill work-group streams the whole segment.
   if (partition_tokens == 0) {
     const int64_t items = static_cast<int64_t>(num_seqs) * P.units * (P.q_blocks > 0 ? P.q_blocks : 1);
-    const int64_t want = 2 * resident_work_groups(2, PKV_BF16);
+    const int64_t want = 2 * kComputeUnits * 3;  // 3 prefill work-groups fit a compute unit
     int32_t cover = 16;
     while (cover < max_blocks_per_seq) cover *= 2;
     P.bpp = cover;
