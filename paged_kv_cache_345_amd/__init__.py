@@ -113,6 +113,9 @@ SIGNATURES = {
 _LIB = None
 
 
+from . import validate as _validate  # noqa: E402  (host contract checks under PKV_VALIDATE=1)
+
+
 class PagedKVError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -278,6 +281,8 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, num_kv_he
             _gpu(context_lens, "context_lens", torch.int32, 1)]
     if context_lens.shape[0] != num_seqs or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("context_lens / v_cache shape mismatch")
+    if _validate.enabled():
+        _validate.check_tables(block_tables, context_lens, desc.num_blocks)
     need = workspace_size(num_seqs, num_heads, mbps, desc, partition_tokens) if num_seqs else 0
     ws_ptr, ws_bytes = None, 0
     if need:
@@ -306,6 +311,8 @@ def paged_attn_decode_plan(context_lens, num_heads: int, max_blocks_per_seq: int
     torch = _torch()
     desc = _desc_of(k_cache)
     n = int(context_lens.shape[0])
+    if _validate.enabled():
+        _validate.check_lengths(context_lens, max_blocks_per_seq)
     st = lib().paged_attn_decode_plan(_gpu(context_lens, "context_lens", torch.int32, 1), n, int(num_heads),
                                       int(max_blocks_per_seq), ctypes.byref(desc), int(partition_tokens),
                                       _gpu(workspace, "workspace"), workspace.numel() * workspace.element_size(),
@@ -384,6 +391,9 @@ def paged_attn_prefill(out, q, k_cache, v_cache, block_tables, context_lens, que
     if fp8 != (k_scale is not None and v_scale is not None):
         raise ValueError("an fp8 cache needs k_scale and v_scale, a 16-bit cache takes neither")
     cache_dtype = torch.uint8 if fp8 else q.dtype
+    if _validate.enabled():
+        _validate.check_tables(block_tables, context_lens, desc.num_blocks)
+        _validate.check_query_start(query_start, context_lens, tq, max_query_len)
     need = prefill_workspace_size(num_seqs, num_heads, mbps, tq, max_query_len, desc, partition_tokens)
     ws_ptr, ws_bytes = None, 0
     if need:
@@ -413,6 +423,8 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, stream=None):
     n = int(slot_mapping.shape[0])
     if tuple(k.shape) != (n, desc.num_kv_heads, HEAD_SIZE) or tuple(v.shape) != tuple(k.shape):
         raise ValueError("k, v must be [num_tokens, num_kv_heads, 128]")
+    if _validate.enabled():
+        _validate.check_slots(slot_mapping, desc.num_blocks)
     st = lib().reshape_and_cache(_gpu(k, "k", k_cache.dtype), _gpu(v, "v", k_cache.dtype),
                                  _gpu(k_cache, "k_cache"), _gpu(v_cache, "v_cache", k_cache.dtype),
                                  _gpu(slot_mapping, "slot_mapping", torch.int32, 1), n, ctypes.byref(desc),
@@ -428,6 +440,8 @@ def reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, k_scale: float, 
     n = int(slot_mapping.shape[0])
     if tuple(k.shape) != (n, desc.num_kv_heads, HEAD_SIZE) or tuple(v.shape) != tuple(k.shape):
         raise ValueError("k, v must be [num_tokens, num_kv_heads, 128]")
+    if _validate.enabled():
+        _validate.check_slots(slot_mapping, desc.num_blocks)
     sc = fp8_scales(k.dtype, k_scale, v_scale)
     st = lib().reshape_and_cache_fp8(_gpu(k, "k"), _gpu(v, "v", k.dtype), _gpu(k_cache, "k_cache", torch.uint8),
                                      _gpu(v_cache, "v_cache", torch.uint8),
@@ -445,6 +459,8 @@ def copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
     n = int(block_pairs.shape[0])
     if n == 0:
         return
+    if _validate.enabled():
+        _validate.check_copy_pairs(block_pairs, desc.num_blocks)
     st = lib().copy_blocks(_gpu(k_cache, "k_cache"), _gpu(v_cache, "v_cache", k_cache.dtype),
                            _gpu(block_pairs, "block_pairs", torch.int32, 2), n, ctypes.byref(desc),
                            _stream_handle(stream))
@@ -470,6 +486,8 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, *, stream=None):
     n = int(block_pairs.shape[0])
     if n == 0:
         return
+    if _validate.enabled():
+        _validate.check_swap_pairs(block_pairs, sd.num_blocks, dd.num_blocks)
     st = lib().swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), ctypes.byref(dd), src_k.data_ptr(), src_v.data_ptr(),
                            ctypes.byref(sd), block_pairs.data_ptr(), n, _stream_handle(stream))
     _check(st, "swap_blocks")
@@ -480,6 +498,8 @@ def gather_cache(k_out, v_out, k_cache, v_cache, block_tables, context_lens, out
     torch = _torch()
     desc = _desc_of(k_cache)
     num_seqs, mbps = block_tables.shape
+    if _validate.enabled():
+        _validate.check_tables(block_tables, context_lens, desc.num_blocks)
     st = lib().gather_cache(_gpu(k_out, "k_out", k_cache.dtype), _gpu(v_out, "v_out", k_cache.dtype),
                             _gpu(k_cache, "k_cache"), _gpu(v_cache, "v_cache", k_cache.dtype),
                             _gpu(block_tables, "block_tables", torch.int32, 2),

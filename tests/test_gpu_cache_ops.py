@@ -118,3 +118,34 @@ def test_full_size_llama13b_step_sampled():
         k, v = wl.seq_kv(s)
         assert np.array_equal(kh[offs[i]:offs[i] + lens[i]], k.view(np.uint16)), s
         assert np.array_equal(vh[offs[i]:offs[i] + lens[i]], v.view(np.uint16)), s
+
+
+def test_validate_mode_catches_contract_violations(monkeypatch):
+    """With PKV_VALIDATE=1 the binding checks device-array contents on host
+    copies and raises before launching; valid calls run unchanged."""
+    monkeypatch.setenv("PKV_VALIDATE", "1")
+    wl = synth.make_workload("tiny")
+    step = harness.build_step(wl, run=False)
+    step.copy()
+    step.write()
+    out = step.decode()
+    torch.cuda.synchronize()
+    ref = harness.to_host_bits(out).copy()
+    bad = step.block_tables.clone()
+    bad[0, 0] = wl.pool_blocks  # outside the pool
+    with pytest.raises(ValueError, match="block_tables"):
+        step.decode(out=torch.empty_like(out), block_tables=bad)
+    lens = step.context_lens.clone()
+    lens[1] = 0
+    with pytest.raises(ValueError, match="context_lens"):
+        pkv.paged_attn_decode(torch.empty_like(out), step.q, step.k_cache, step.v_cache, step.block_tables, lens,
+                              wl.scale, wl.num_kv_heads)
+    dup = step.slot_mapping.clone()
+    dup[1] = dup[0]
+    with pytest.raises(ValueError, match="twice"):
+        pkv.reshape_and_cache(step.k_new, step.v_new, step.k_cache, step.v_cache, dup)
+    with pytest.raises(ValueError, match="source and a destination"):
+        pkv.copy_blocks(step.k_cache, step.v_cache, torch.tensor([[0, 1], [1, 2]], dtype=torch.int32).cuda())
+    out2 = step.decode(out=torch.empty_like(out))  # the caches were not touched by the refused calls
+    torch.cuda.synchronize()
+    assert np.array_equal(harness.to_host_bits(out2), ref)
