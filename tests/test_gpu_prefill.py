@@ -140,3 +140,69 @@ def test_full_size_sampled(name):
                 ref = oracle.attention_ref(q[h:h + 1], kf[:p + 1, h // g:h // g + 1], vf[:p + 1, h // g:h // g + 1],
                                            wl.scale)[0]
                 assert np.abs(got[qs[s] + j, h] - ref).max() <= TOL[wl.dtype], (s, j, h)
+
+
+@pytest.mark.parametrize("dtype,g,pt,kv", [("fp16", 1, 256, None), ("bf16", 4, 0, None), ("bf16", 8, 512, None),
+                                           ("fp16", 2, 0, "fp8e4m3"), ("bf16", 16, 256, "fp8e4m3")])
+def test_long_chunks_sampled(dtype, g, pt, kv):
+    """Chunks of hundreds of queries over contexts of one to two thousand
+    tokens: many 2-block steps per work-group, the mask-free path between the
+    diagonal steps, segments merged by the reduce when pt forces them.  Every
+    output is finite; the first, last and every 37th query of each sequence,
+    for sampled heads, match the oracle."""
+    hkv = 2
+    wl = synth.make_prefill_workload(8400 + g + (kv is not None), num_seqs=3, num_heads=hkv * g, num_kv_heads=hkv,
+                                     dtype=dtype, context=(900, 2100), chunk=(300, 700), kv_dtype=kv,
+                                     k_scale=0.0125, v_scale=0.02)
+    pre = harness.build_prefill(wl, partition_tokens=pt)
+    got = _out_f64(pre.out, dtype)
+    assert np.isfinite(got).all()
+    heads = sorted({0, wl.num_heads - 1, wl.num_heads // 2})
+    qs = wl.query_start
+    for s in range(wl.num_seqs):
+        C = int(wl.chunk_lens[s])
+        rows = sorted(set(range(0, C, 37)) | {C - 1})
+        ref = _ref_rows_at(wl, s, rows, heads)
+        for (j, h), r in ref.items():
+            assert np.abs(got[qs[s] + j, h] - r).max() <= TOL[dtype], (s, j, h)
+
+
+@pytest.mark.parametrize("dtype,kv", [("fp16", None), ("bf16", "fp8e4m3")])
+def test_whole_long_prompts(dtype, kv):
+    """Chunk = the whole context (plain causal prefill) for prompts of 700 to
+    1000 tokens: the causal diagonal crosses every step of the work-groups."""
+    wl = synth.make_prefill_workload(8500 + (kv is not None), num_seqs=2, num_heads=8, num_kv_heads=2, dtype=dtype,
+                                     context=(700, 1000), chunk=(1, 1), kv_dtype=kv, k_scale=0.0125, v_scale=0.02)
+    wl.chunk_lens[:] = wl.context_lens
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((int(wl.chunk_lens.sum()), wl.num_heads, 128)).astype(np.float32)
+    wl.q = synth.round_fp16(q) if dtype == "fp16" else synth.round_bf16_bits(q)
+    pre = harness.build_prefill(wl)
+    got = _out_f64(pre.out, dtype)
+    assert np.isfinite(got).all()
+    qs = wl.query_start
+    for s in range(wl.num_seqs):
+        C = int(wl.chunk_lens[s])
+        rows = sorted(set(range(0, C, 53)) | {1, 15, 16, 17, 31, 32, 127, 128, C - 1})
+        for (j, h), r in _ref_rows_at(wl, s, rows, [0, 3, 5, 7]).items():
+            assert np.abs(got[qs[s] + j, h] - r).max() <= TOL[dtype], (s, j, h)
+
+
+def _ref_rows_at(wl, s, rows, heads):
+    """Oracle rows {(chunk query j, head): float64 [128]} of sequence s."""
+    g = wl.num_heads // wl.num_kv_heads
+    k, v = wl.seq_kv(s)
+    if wl.kv_dtype == "fp8e4m3":
+        kf = ofp8.e4m3_decode(ofp8.quantize_ref(k, wl.dtype, wl.k_scale)) * np.float64(np.float32(wl.k_scale))
+        vf = ofp8.e4m3_decode(ofp8.quantize_ref(v, wl.dtype, wl.v_scale)) * np.float64(np.float32(wl.v_scale))
+    else:
+        kf, vf = oracle.to_f64(k, wl.dtype), oracle.to_f64(v, wl.dtype)
+    L, C = int(wl.context_lens[s]), int(wl.chunk_lens[s])
+    out = {}
+    for j in rows:
+        p = L - C + j
+        q = oracle.to_f64(wl.q[wl.query_start[s] + j], wl.dtype)
+        for h in heads:
+            out[(j, h)] = oracle.attention_ref(q[h:h + 1], kf[:p + 1, h // g:h // g + 1], vf[:p + 1, h // g:h // g + 1],
+                                               wl.scale)[0]
+    return out
