@@ -28,8 +28,33 @@ SOURCES = ["api.hip", "decode.hip", "prefill.hip", "plan.hip", "cache_ops.hip", 
 COMMON = ["-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-fgpu-flush-denormals-to-zero", "-munsafe-fp-atomics"]
-# Extra flags per source file (none at present).
-PER_SOURCE_FLAGS: dict = {}
+# Extra flags per source file.  prefill.hip: the compiler's resource report,
+# checked below.
+PER_SOURCE_FLAGS: dict = {"prefill.hip": ["-Rpass-analysis=kernel-resource-usage"]}
+
+# Kernels that must use no per-lane scratch memory.  The prefill kernel keeps
+# the vector-memory counter itself around its LDS loads; a spill would add
+# scratch loads and stores to its step loop that the counts do not include.
+NO_SCRATCH = {"prefill.hip": "prefill_kernel"}
+
+
+def _check_no_scratch(src: str, remarks: str) -> None:
+    """Fail the build when a kernel listed in NO_SCRATCH reports scratch use."""
+    kernel = NO_SCRATCH.get(src)
+    if not kernel:
+        return
+    seen, fn = 0, None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            fn = line.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in line and fn and kernel in fn:
+            seen += 1
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if size != 0:
+                raise RuntimeError(f"{fn} uses {size} bytes of scratch per lane; its step loop must not "
+                                   f"(see the vector-memory counting in {src})")
+    if seen == 0:
+        raise RuntimeError(f"no resource report for {kernel} in the output of {src}")
 
 
 def hipcc() -> str:
@@ -51,6 +76,7 @@ def _compile(src: str, verbose: bool) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{r.stdout}\n{r.stderr}")
+    _check_no_scratch(src, r.stderr)
     return obj
 
 

@@ -266,3 +266,18 @@ def test_fp8_argument_errors_return_before_launch():
     assert L.reshape_and_cache_fp8(p, p, p, p, p, 4, ctypes.byref(d8), _scales(ks=0.0), None) == pkv.PKV_ERR_INVALID
     assert L.reshape_and_cache_fp8(p, p, p, p, p, -1, ctypes.byref(d8), _scales(), None) == pkv.PKV_ERR_INVALID
     assert L.reshape_and_cache_fp8(None, None, None, None, None, 0, ctypes.byref(d8), _scales(), None) == pkv.PKV_OK
+
+
+def test_build_refuses_a_prefill_kernel_with_scratch():
+    """The build reads the compiler's resource report for prefill.hip and
+    fails when the prefill kernel uses per-lane scratch (its step loop counts
+    its own vector-memory operations)."""
+    from paged_kv_cache_345_amd import build as b
+    ok = ("f.hip:1:1: remark: Function Name: _ZN3pkv14prefill_kernelINS_3F16EEEv\n"
+          "f.hip:1:1: remark:     ScratchSize [bytes/lane]: 0\n")
+    b._check_no_scratch("prefill.hip", ok)
+    b._check_no_scratch("decode.hip", "")  # not listed: not checked
+    with pytest.raises(RuntimeError, match="scratch"):
+        b._check_no_scratch("prefill.hip", ok.replace("]: 0", "]: 32"))
+    with pytest.raises(RuntimeError, match="no resource report"):
+        b._check_no_scratch("prefill.hip", "")
