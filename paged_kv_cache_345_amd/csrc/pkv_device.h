@@ -168,16 +168,24 @@ __device__ inline float lane_from(float x, int src_lane) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
 }
 
-// sum / max over the 4 rows (lanes l, l^16, l^32, l^48), result in every lane
+// sum / max over the 4 rows (lanes l, l^16, l^32, l^48), result in every lane.
+// gfx950's row-swap permutes do the two exchanges in the vector ALU: with both
+// operands x, v_permlane16_swap leaves (rows 0,0,2,2) in one result and (rows
+// 1,1,3,3) in the other, so combining them pairs lane l with l^16;
+// v_permlane32_swap does the same for the two halves (l with l^32).  The
+// pairing, and so every rounded sum, is that of the shuffle form
+// (x + x^16) + (x^32 + x^48); shuffles by lane would go through LDS.
 __device__ inline float cross_row_sum(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ inline float cross_row_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Buffer descriptor covering one 4 KiB page (gfx9 descriptor word 3:
