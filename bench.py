@@ -208,7 +208,8 @@ def prefill_bench(args, name: str) -> int:
         "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype if wl.kv_dtype is None else f"{wl.dtype} ({wl.kv_dtype} cache)", "data": "synthetic",
         "config": {"workload": wl.description, "name": name, "num_seqs": wl.num_seqs, "num_heads": wl.num_heads,
                    "num_kv_heads": wl.num_kv_heads, "head_size": 128, "block_size": 16,
                    "context_tokens": int(L.sum()), "query_tokens": int(C.sum()),

@@ -484,6 +484,11 @@ PREFILL_CONFIGS = {
                              context=(1024, 4096), chunk=(512, 512),
                              description="chunked prefill, LLaMA-13B-shaped: 16 seqs, 40 MHA heads, fp16, "
                                          "contexts U[1024,4096], the last 512 tokens of each as the chunk"),
+    "prefill_llama13b_fp8": dict(seed=21, num_seqs=16, num_heads=40, num_kv_heads=40, dtype="fp16",
+                                 context=(1024, 4096), chunk=(512, 512), kv_dtype="fp8e4m3", k_scale=0.0125,
+                                 v_scale=0.0125,
+                                 description="chunked prefill, LLaMA-13B-shaped, over an fp8 (E4M3) cache: 16 seqs, "
+                                             "40 MHA heads, fp16 queries, contexts U[1024,4096], 512-token chunks"),
     "prefill_gqa": dict(seed=22, num_seqs=16, num_heads=64, num_kv_heads=8, dtype="bf16",
                         context=(1024, 8192), chunk=(512, 512), key_scale=(0.5, 2.0),
                         description="chunked prefill, GQA: 16 seqs, 64 query / 8 KV heads, bf16, "

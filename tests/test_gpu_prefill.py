@@ -115,7 +115,8 @@ def test_fp8_cache(dtype, g):
         assert np.abs(got[row, h] - ref).max() <= TOL[dtype], (row, h)
 
 
-FULL = {"prefill_llama13b": ([0, 5, 15], [0, 17, 39]), "prefill_gqa": ([0, 9, 15], [0, 7, 8, 63])}
+FULL = {"prefill_llama13b": ([0, 5, 15], [0, 17, 39]), "prefill_gqa": ([0, 9, 15], [0, 7, 8, 63]),
+        "prefill_llama13b_fp8": ([0, 15], [0, 39])}
 
 
 @pytest.mark.parametrize("name", sorted(FULL))
@@ -128,18 +129,10 @@ def test_full_size_sampled(name):
     assert np.isfinite(got).all()
     seqs, heads = FULL[name]
     qs = wl.query_start
-    g = wl.num_heads // wl.num_kv_heads
     for s in seqs:
-        k, v = wl.seq_kv(s)
-        kf, vf = oracle.to_f64(k, wl.dtype), oracle.to_f64(v, wl.dtype)
-        L, C = int(wl.context_lens[s]), int(wl.chunk_lens[s])
-        for j in (0, C // 2, C - 1):
-            p = L - C + j
-            q = oracle.to_f64(wl.q[qs[s] + j], wl.dtype)
-            for h in heads:
-                ref = oracle.attention_ref(q[h:h + 1], kf[:p + 1, h // g:h // g + 1], vf[:p + 1, h // g:h // g + 1],
-                                           wl.scale)[0]
-                assert np.abs(got[qs[s] + j, h] - ref).max() <= TOL[wl.dtype], (s, j, h)
+        C = int(wl.chunk_lens[s])
+        for (j, h), ref in _ref_rows_at(wl, s, [0, C // 2, C - 1], heads).items():
+            assert np.abs(got[qs[s] + j, h] - ref).max() <= TOL[wl.dtype], (s, j, h)
 
 
 @pytest.mark.parametrize("dtype,g,pt,kv", [("fp16", 1, 256, None), ("bf16", 4, 0, None), ("bf16", 8, 512, None),
