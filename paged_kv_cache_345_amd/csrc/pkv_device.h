@@ -91,6 +91,8 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a), __builtin_bit_cast(half4_t, b), c,
                                                  0, 0, 0);
   }
+  // the same product over 8 tokens per lane (two V fragments side by side)
+  __device__ static inline float4_t mfma_pv32(uint4 a, uint4 b, float4_t c) { return mfma_qk(a, b, c); }
 };
 
 struct BF16 {
@@ -118,6 +120,7 @@ struct BF16 {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a), __builtin_bit_cast(short4_t, b),
                                                      c, 0, 0, 0);
   }
+  __device__ static inline float4_t mfma_pv32(uint4 a, uint4 b, float4_t c) { return mfma_qk(a, b, c); }
 };
 
 template <class DT>

@@ -18,7 +18,8 @@ namespace pkv {
 // every wave reads its fragments from there for both of its tiles.  Per step
 // and tile: S = K Q^T (16x16x32 products), one online-softmax update over the
 // step's keys (the causal mask by row position is evaluated only in steps
-// that reach past some row's position), then O += P V (16x16x16 products).
+// that reach past some row's position), then O += P V (16x16x32 products over
+// the step's two blocks).
 // A block wholly past every position of a wave is skipped by that wave.  Each
 // wave writes its own rows.
 //
@@ -62,6 +63,11 @@ struct LdsPage<Page16> {
     for (int i = 0; i < 4; ++i) kv[i] = *reinterpret_cast<const uint4*>(pg + 1024 * i + 16 * lane);
   }
   __device__ static inline void v(const char* pg, int lane, uint4 (&vv)[4]) { k(pg, lane, vv); }
+  // V fragments 2 h and 2 h + 1
+  __device__ static inline void v_half(const char* pg, int lane, int h, uint4& f0, uint4& f1) {
+    f0 = *reinterpret_cast<const uint4*>(pg + 2048 * h + 16 * lane);
+    f1 = *reinterpret_cast<const uint4*>(pg + 2048 * h + 1024 + 16 * lane);
+  }
 };
 template <class DT>
 struct LdsPage<PageFp8<DT>> {
@@ -72,6 +78,9 @@ struct LdsPage<PageFp8<DT>> {
     PageFp8<DT>::widen(w1, kv[2], kv[3]);
   }
   __device__ static inline void v(const char* pg, int lane, uint4 (&vv)[4]) { k(pg, lane, vv); }
+  __device__ static inline void v_half(const char* pg, int lane, int h, uint4& f0, uint4& f1) {
+    PageFp8<DT>::widen(*reinterpret_cast<const uint4*>(pg + 1024 * h + 16 * lane), f0, f1);
+  }
 };
 
 // s_waitcnt vmcnt(min(n, kMax) * kPerStep): at most n steps of kPerStep loads
@@ -320,20 +329,50 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
       }
     }
 
-    // O += P V
+    // O += P V over both blocks of the step in one 16x16x32 product per
+    // (tile, 16 dims): lane (grp, col) gives k slots 8 grp .. 8 grp + 3 to
+    // tokens 4 grp .. 4 grp + 3 of the first block and k slots 8 grp + 4 ..
+    // 8 grp + 7 to the same tokens of the second, in P and in V alike.  A block
+    // outside the step's live prefix has P = 0 and V = 0 (its LDS copy may hold
+    // stale slots of the sequence's last block, NaN included).
+    static_assert(kStageBlocks == 2, "one 16x16x32 product spans the step's two blocks");
+    // word masks of the V fragments (mask_v's): stale slots past the context and
+    // a dead second block read as zeros
+    uint32_t mk01[kStageBlocks], mk23[kStageBlocks];
 #pragma unroll
     for (int b = 0; b < kStageBlocks; ++b) {
-      if (!kFast && b >= n) continue;
-      uint4 vv[4];
-      LdsPage<PF>::v(lds[buf][1][b], lane, vv);
-      const int nvalid = L - (jstep + b) * kBlockSize;
-      if (!kFast && nvalid < kBlockSize) mask_v(vv, grp, nvalid);  // stale slots past the context
+      const int nvalid = (kFast || b < n) ? L - (jstep + b) * kBlockSize : 0;
+      const int t0 = 4 * grp;
+      mk01[b] = (kFast || t0 + 0 < nvalid ? 0x0000ffffu : 0u) | (kFast || t0 + 1 < nvalid ? 0xffff0000u : 0u);
+      mk23[b] = (kFast || t0 + 2 < nvalid ? 0x0000ffffu : 0u) | (kFast || t0 + 3 < nvalid ? 0xffff0000u : 0u);
+    }
+    uint4 pk[kPrefillTiles];  // P of both blocks in the k-slot order above
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd) {
-        const uint4& f = vv[jd >> 1];
-        const uint2 bv = (jd & 1) ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y);
+    for (int T = 0; T < kPrefillTiles; ++T) pk[T] = make_uint4(P[T][0].x, P[T][0].y, P[T][1].x, P[T][1].y);
 #pragma unroll
-        for (int T = 0; T < kPrefillTiles; ++T) O[T][jd] = DT::mfma_pv(P[T][b], bv, O[T][jd]);
+    for (int h = 0; h < 2; ++h) {
+      uint4 f[kStageBlocks][2];
+#pragma unroll
+      for (int b = 0; b < kStageBlocks; ++b) {
+        LdsPage<PF>::v_half(lds[buf][1][b], lane, h, f[b][0], f[b][1]);
+        if (!kFast) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            f[b][e].x &= mk01[b];
+            f[b][e].y &= mk23[b];
+            f[b][e].z &= mk01[b];
+            f[b][e].w &= mk23[b];
+          }
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int jd = 4 * h + jj;
+        const uint4& f0 = f[0][jj >> 1];
+        const uint4& f1 = f[1][jj >> 1];
+        const uint4 bv = (jj & 1) ? make_uint4(f0.z, f0.w, f1.z, f1.w) : make_uint4(f0.x, f0.y, f1.x, f1.y);
+#pragma unroll
+        for (int T = 0; T < kPrefillTiles; ++T) O[T][jd] = DT::mfma_pv32(pk[T], bv, O[T][jd]);
       }
     }
   };
