@@ -52,6 +52,80 @@ __device__ inline int prefill_wg_blocks(const PrefillArgs& pa, int L, int C, int
   return (L - C + last_q) / kBlockSize + 1;
 }
 
+// Work order.  Work-groups differ in length by the number of blocks they
+// stream, and about three rounds of them fill the chip, so the dispatch order
+// decides how long the last ones run alone.  Up to kPrefillSortSeqs sequences,
+// each unit's sequences go out longest first: a group is (unit, sequence)
+// with its q_blocks x parts_max items (latest query block first, so the
+// longest item of the group leads), groups run in the order (unit, sequences
+// by block count descending, ties by index), and the XCDs take 8 contiguous
+// chunks of that order.  An XCD thus works on one or two units at a time, and
+// sequences that share prompt blocks read the shared pages in one L2 at about
+// the same time (dealing consecutive groups to different XCDs instead put
+// five units on each XCD at once and made a batch of prompts that share a
+// 1024-token prefix 9% slower).  Longer batches keep the plain order (unit,
+// sequence, query block, segment) in 8 contiguous XCD chunks.
+constexpr int kPrefillSortSeqs = 256;
+
+__host__ __device__ inline int64_t prefill_grid(const PrefillArgs& pa) {
+  const DecodeArgs& a = pa.d;
+  const int64_t per_group = static_cast<int64_t>(pa.q_blocks) * a.parts_max;
+  const int64_t groups = static_cast<int64_t>(a.units) * a.num_seqs;
+  if (a.num_seqs <= kPrefillSortSeqs) return (groups + kNumXcd - 1) / kNumXcd * per_group * kNumXcd;
+  return (groups * per_group + kNumXcd - 1) / kNumXcd * kNumXcd;
+}
+
+// The item of this work-group in the longest-first order: false when the
+// work-group has none (uniform).  Every thread of the work-group calls it.
+__device__ inline bool prefill_sorted_item(const PrefillArgs& pa, int& g, int& qb, int& s, int& u) {
+  const DecodeArgs& a = pa.d;
+  __shared__ __attribute__((aligned(16))) int keys[kPrefillSortSeqs];
+  __shared__ int pick;
+  const int S = a.num_seqs;
+  const int per_group = pa.q_blocks * a.parts_max;
+  const int64_t groups = static_cast<int64_t>(S) * a.units;
+  const int64_t per_xcd = (groups + kNumXcd - 1) / kNumXcd;  // groups per XCD chunk
+  const int64_t xcd = blockIdx.x % kNumXcd;
+  const int i = static_cast<int>(blockIdx.x / kNumXcd);      // item index within the XCD's chunk
+  if (i / per_group >= per_xcd) return false;
+  const int64_t group = xcd * per_xcd + i / per_group;
+  if (group >= groups) return false;
+  u = static_cast<int>(group / S);
+  const int rank = static_cast<int>(group % S);
+  const int m = i % per_group;
+  qb = pa.q_blocks - 1 - m / a.parts_max;
+  g = m % a.parts_max;
+  // sort key of sequence t: blocks of its key range (0 without a chunk);
+  // slots S .. 4 ceil(S/4) - 1 hold -1, which no sequence ranks behind
+  const int t = threadIdx.x;
+  int key = -1;
+  if (t < S) {
+    const int Lt = clamped_len(a, t);
+    const int q0t = pa.query_start[t];
+    const int Ct = min(max(pa.query_start[t + 1] - q0t, 0), Lt);
+    key = Ct > 0 ? (Lt - 1) / kBlockSize + 1 : 0;
+  }
+  if (t < ((S + 3) & ~3)) keys[t] = key;
+  if (t == 0) pick = 0;
+  __syncthreads();
+  // rank of sequence t: the sequences with a larger key, or an equal key and
+  // a lower index, come first; the ranks are a permutation of 0 .. S-1
+  if (t < S) {
+    int r = 0;
+    for (int j = 0; j < S; j += 4) {
+      const int4 k4 = *reinterpret_cast<const int4*>(&keys[j]);
+      r += (k4.x > key) | ((k4.x == key) & (j + 0 < t));
+      r += (k4.y > key) | ((k4.y == key) & (j + 1 < t));
+      r += (k4.z > key) | ((k4.z == key) & (j + 2 < t));
+      r += (k4.w > key) | ((k4.w == key) & (j + 3 < t));
+    }
+    if (r == rank) pick = t;
+  }
+  __syncthreads();
+  s = pick;
+  return true;
+}
+
 // Fragment reads from a page copy in LDS, in the page formats' register layout
 // (lane l's 16 bytes of wave load i sit at byte 1024 i + 16 l of the page).
 template <class PF>
@@ -106,18 +180,23 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
   __shared__ __attribute__((aligned(16))) char lds[kStageBufs][2][kStageBlocks][kPage];  // [buffer][K, V][block]
 
   const DecodeArgs& a = pa.d;
-  // item (unit, sequence, query block, segment), segment fastest; XCD-aware
-  // chunks as in decode's direct mode
-  const int64_t total = static_cast<int64_t>(a.units) * a.num_seqs * pa.q_blocks * a.parts_max;
-  const int64_t per_xcd = (total + kNumXcd - 1) / kNumXcd;
-  const int64_t lam = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
-  if (lam >= total) return;  // uniform over the work-group
-  const int g = static_cast<int>(lam % a.parts_max);
-  int64_t rest = lam / a.parts_max;
-  const int qb = static_cast<int>(rest % pa.q_blocks);
-  rest /= pa.q_blocks;
-  const int s = static_cast<int>(rest % a.num_seqs);
-  const int u = static_cast<int>(rest / a.num_seqs);
+  int g, qb, s, u;  // item: segment, query block, sequence, unit
+  if (a.num_seqs <= kPrefillSortSeqs) {
+    if (!prefill_sorted_item(pa, g, qb, s, u)) return;  // uniform over the work-group
+  } else {
+    // (unit, sequence, query block, segment), segment fastest, in XCD-aware
+    // chunks as in decode's direct mode
+    const int64_t total = static_cast<int64_t>(a.units) * a.num_seqs * pa.q_blocks * a.parts_max;
+    const int64_t per_xcd = (total + kNumXcd - 1) / kNumXcd;
+    const int64_t lam = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
+    if (lam >= total) return;  // uniform over the work-group
+    g = static_cast<int>(lam % a.parts_max);
+    int64_t rest = lam / a.parts_max;
+    qb = static_cast<int>(rest % pa.q_blocks);
+    rest /= pa.q_blocks;
+    s = static_cast<int>(rest % a.num_seqs);
+    u = static_cast<int>(rest / a.num_seqs);
+  }
   const int kvh = u / a.head_tiles;
   const int tile = u - kvh * a.head_tiles;
   const int h0 = kvh * a.group + tile * 16;
@@ -468,8 +547,7 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs pa) {
 template <class DT, class PF>
 static hipError_t launch_prefill_t(const PrefillArgs& pa, hipStream_t stream) {
   const DecodeArgs& a = pa.d;
-  const int64_t total = static_cast<int64_t>(a.units) * a.num_seqs * pa.q_blocks * a.parts_max;
-  const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+  const int64_t grid = prefill_grid(pa);
   if (grid > 0x7fffffff || grid <= 0) return hipErrorInvalidValue;
   prefill_kernel<DT, PF><<<dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream>>>(pa);
   hipError_t err = hipGetLastError();
