@@ -262,47 +262,48 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
     for (int i = 0; i < 4; ++i)
       asm volatile("" : "+v"(qf[T][i].x), "+v"(qf[T][i].y), "+v"(qf[T][i].z), "+v"(qf[T][i].w));
 
-  // step loads, straight from the cache into LDS: wave w makes the step's
-  // 1 KiB pieces kLoads w .. kLoads w + kLoads - 1 (piece p: page p / kPieces,
-  // K pages first, then V; lane l's 16 bytes land at byte 16 l of the piece)
+  // step loads, straight from the cache into LDS: wave w loads page w of the
+  // step (the K pages of its blocks first, then the V pages) as kLoads 1 KiB
+  // pieces; lane l's 16 bytes of piece i land at byte 1024 i + 16 l of the copy
   const int32_t* brow = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq + j0;
   const int64_t page_stride = static_cast<int64_t>(a.num_kv_heads) * kPage;
   const int64_t head_off = static_cast<int64_t>(kvh) * kPage;
   const char* kc = reinterpret_cast<const char*>(a.k_cache);
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
+  static_assert(kLoads == kPieces, "each wave loads one whole page per step");
+  const bool k_wave = wave < kStageBlocks;  // waves 0, 1: K pages; waves 2, 3: V pages
+  const char* const cache_base = (k_wave ? kc : vc) + head_off;
+  const int wave_blk = wave % kStageBlocks;  // the step's block this wave loads
   auto issue = [&](int st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int p = kLoads * wave + i;
-      const int pg = p / kPieces;
-      const int b = pg % kStageBlocks;
-      const int jj = st * kStageBlocks + b;
-      // block id by a scalar load (the asm memory clobbers below keep the
-      // compiler from proving the table unchanged, so it would use a vector
-      // load and a wait that also drains the step loads in flight)
-      int bid;
-      asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
-                   : "=s"(bid) : "s"(brow + min(jj, nb - 1)) : "memory");
-      const bool bad = jj >= nb || static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks);
-      const char* page = (pg < kStageBlocks ? kc : vc) + (bad ? 0 : bid) * page_stride + head_off;
-      const __amdgpu_buffer_rsrc_t r = range_rsrc(page, bad ? 0 : kPage);  // a bad id reads zeros
-      // LDS byte address of the piece (the low 32 bits of its generic address)
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-          reinterpret_cast<uintptr_t>(&lds[st % kStageBufs][pg / kStageBlocks][b][1024 * (p % kPieces)])));
-      const uint32_t off = 1024u * (p % kPieces) + 16u * lane;
-      // K: non-temporal, V: default policy, as in the decode page loads.  The
-      // load goes to LDS (lane l's 16 bytes at dst + 16 l) and is counted by the
-      // vector-memory counter, which wait_steps below checks.
+    const int jj = st * kStageBlocks + wave_blk;
+    // block id by a scalar load (the asm memory clobbers below keep the
+    // compiler from proving the table unchanged, so it would use a vector
+    // load and a wait that also drains the step loads in flight)
+    int bid;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                 : "=s"(bid) : "s"(brow + min(jj, nb - 1)) : "memory");
+    const bool bad = jj >= nb || static_cast<unsigned>(bid) >= static_cast<unsigned>(a.num_blocks);
+    const __amdgpu_buffer_rsrc_t r =
+        range_rsrc(cache_base + (bad ? 0 : bid) * page_stride, bad ? 0 : kPage);  // a bad id reads zeros
+    // LDS byte address of the page copy (the low 32 bits of its generic address)
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>(&lds[st % kStageBufs][wave / kStageBlocks][wave_blk][0])));
+    // K: non-temporal, V: default policy, as in the decode page loads.  Load i
+    // goes to LDS (lane l's 16 bytes at dst + 1024 i + 16 l) and is counted by
+    // the vector-memory counter, which wait_steps below checks.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // M0 is written here and read by nothing else
-      if (pg < kStageBlocks)
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const uint32_t off = 1024u * i + 16u * lane;
+      if (k_wave)
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-                     :: "s"(dst), "v"(off), "s"(r) : "memory", "m0");
+                     :: "s"(dst + 1024u * i), "v"(off), "s"(r) : "memory", "m0");
       else
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :: "s"(dst), "v"(off), "s"(r) : "memory", "m0");
-#pragma clang diagnostic pop
+                     :: "s"(dst + 1024u * i), "v"(off), "s"(r) : "memory", "m0");
     }
+#pragma clang diagnostic pop
   };
   // Work-group barrier between steps.  Before it each wave has waited for its
   // own loads of the step about to be read (wait_steps) and for its own LDS
