@@ -304,9 +304,10 @@ pkv_status paged_attn_decode_run_fp8(void* out, const void* q, const void* k_cac
  *                    partials per (query token, head) when a work-group's key
  *                    range spans several segments; its size is
  *                    paged_attn_prefill_workspace_size().
- * One work-group takes 64 (query position, head) rows of one KV head (16 per
- * wave) and streams the keys up to its last position on the matrix cores;
- * keys beyond a row's position are masked.  Tolerance and errors as decode.
+ * One work-group takes 128 (query position, head) rows of one KV head (two
+ * 16-row tiles per wave) and streams the keys up to its last position on the
+ * matrix cores; keys beyond a row's position are masked.  Tolerance and
+ * errors as decode.
  * ------------------------------------------------------------------------- */
 size_t paged_attn_prefill_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                          int32_t num_query_tokens, int32_t max_query_len,
