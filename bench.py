@@ -472,6 +472,8 @@ def main() -> int:
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="decode workloads: also time the step captured in a HIP graph and replayed")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the bench, run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -543,6 +545,28 @@ def main() -> int:
     log(f"step {ms_per_step * 1e3:.1f} us (wall {wall_s / K * 1e6:.1f} us); decode avg {dec_avg * 1e3:.1f} us, "
         f"min {min(dec_ms) * 1e3:.1f} us")
 
+    graph_us = None
+    if args.graph:
+        # the same step captured once in a HIP graph and replayed: no host
+        # launch work between the kernels
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step.copy()
+            step.write()
+            step.plan()
+            step.run()
+        for _ in range(args.warmup):
+            graph.replay()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record()
+        for _ in range(K):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) / K * 1e3
+        log(f"graph replay: step {graph_us:.1f} us")
+
     seg_tokens = pkv.partition_tokens_for(wl.num_seqs, wl.num_heads, step.max_blocks, step.desc,
                                           step.partition_tokens)
     step_gbs = nb["step"] / (ms_per_step * 1e-3) / 1e9
@@ -584,6 +608,7 @@ def main() -> int:
         "context_tokens_per_s": round(wl.total_context / (ms_per_step * 1e-3), 1),
         "bytes": nb,
         "decode_call_us": round(dec_avg * 1e3, 2),
+        "graph_step_us": None if graph_us is None else round(graph_us, 2),
         "roofline": {
             "bound": "hbm",
             "kernel": ("paged_attn_decode_run: " + ("decode_mha_kernel" if wl.num_heads == wl.num_kv_heads
