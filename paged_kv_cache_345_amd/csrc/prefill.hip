@@ -261,6 +261,23 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       asm volatile("" : "+v"(qf[T][i].x), "+v"(qf[T][i].y), "+v"(qf[T][i].z), "+v"(qf[T][i].w));
+  // A negative scale is carried by the queries: with q negated (sign bits
+  // flipped, exact) the scores change sign exactly, and S sc = (-S)(-sc), so
+  // every logit keeps its bits while the scale the steps use is >= 0 and the
+  // row maximum of the logits is sc times the row maximum of the scores.
+  const bool neg_scale = a.scale_log2e < 0.f;
+  const float sc = neg_scale ? -a.scale_log2e : a.scale_log2e;
+  if (neg_scale) {
+#pragma unroll
+    for (int T = 0; T < kPrefillTiles; ++T)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qf[T][i].x ^= 0x80008000u;
+        qf[T][i].y ^= 0x80008000u;
+        qf[T][i].z ^= 0x80008000u;
+        qf[T][i].w ^= 0x80008000u;
+      }
+  }
 
   // step loads, straight from the cache into LDS: wave w loads page w of the
   // step (the K pages of its blocks first, then the V pages) as kLoads 1 KiB
@@ -318,7 +335,6 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
     wait_vm_steps<kLoads, kStageBufs - 2>(n);
   };
 
-  const float sc = a.scale_log2e;
   const uint32_t ones = DT::pack2(1.f, 1.f);
   // One step over blocks jstep .. jstep + n - 1 (n >= 1, wave-uniform).  kFast:
   // n == kStageBlocks and every valid row of the wave sees every key, so no
@@ -341,29 +357,27 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
     }
 
     uint2 P[kPrefillTiles][kStageBlocks];
+    float alpha[kPrefillTiles];
+    if (kFast) {
+      // row maxima of the raw scores of both tiles first (sc >= 0: the max of
+      // S sc is sc times the max of S), in one stretch of code
+      float e[kPrefillTiles];
 #pragma unroll
-    for (int T = 0; T < kPrefillTiles; ++T) {
-      float m_new, alpha, zs = 0.f;
-      if (kFast) {
-        // row extreme of the raw scores (the max of S * sc is sc times the
-        // max of S for sc >= 0, the min otherwise)
-        float e = S[T][0][0];
-        if (sc >= 0.f) {
+      for (int T = 0; T < kPrefillTiles; ++T) {
+        e[T] = S[T][0][0];
 #pragma unroll
-          for (int b = 0; b < kStageBlocks; ++b)
+        for (int b = 0; b < kStageBlocks; ++b)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) e = fmaxf(e, S[T][b][r]);
-          e = cross_row_max(e);
-        } else {
+          for (int r = 0; r < 4; ++r) e[T] = fmaxf(e[T], S[T][b][r]);
+      }
 #pragma unroll
-          for (int b = 0; b < kStageBlocks; ++b)
+      for (int T = 0; T < kPrefillTiles; ++T) e[T] = cross_row_max(e[T]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) e = fminf(e, S[T][b][r]);
-          e = -cross_row_max(-e);
-        }
-        m_new = fmaxf(m[T], e * sc);
-        alpha = exp2_fast(m[T] - m_new);
+      for (int T = 0; T < kPrefillTiles; ++T) {
+        const float m_new = fmaxf(m[T], e[T] * sc);
+        alpha[T] = exp2_fast(m[T] - m_new);
         const float neg = -m_new;
+        float zs = 0.f;
 #pragma unroll
         for (int b = 0; b < kStageBlocks; ++b) {
           P[T][b].x = DT::pack2(exp2_fast(fmaf(S[T][b][0], sc, neg)), exp2_fast(fmaf(S[T][b][1], sc, neg)));
@@ -371,7 +385,12 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
           zs = DT::dot2(P[T][b].x, ones, zs);
           zs = DT::dot2(P[T][b].y, ones, zs);
         }
-      } else {
+        m[T] = m_new;
+        z[T] = fmaf(z[T], alpha[T], zs);
+      }
+    } else {
+#pragma unroll
+      for (int T = 0; T < kPrefillTiles; ++T) {
         float x[kStageBlocks][4];
         float bm = kMaskedLogit;
 #pragma unroll
@@ -384,8 +403,9 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
           }
         }
         bm = cross_row_max(bm);
-        m_new = fmaxf(m[T], bm);
-        alpha = exp2_fast(m[T] - m_new);
+        const float m_new = fmaxf(m[T], bm);
+        alpha[T] = exp2_fast(m[T] - m_new);
+        float zs = 0.f;
 #pragma unroll
         for (int b = 0; b < kStageBlocks; ++b) {
           P[T][b].x = DT::pack2(exp2_fast(x[b][0] - m_new), exp2_fast(x[b][1] - m_new));
@@ -393,14 +413,17 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
           zs = DT::dot2(P[T][b].x, ones, zs);
           zs = DT::dot2(P[T][b].y, ones, zs);
         }
+        m[T] = m_new;
+        z[T] = fmaf(z[T], alpha[T], zs);
       }
-      m[T] = m_new;
-      z[T] = fmaf(z[T], alpha, zs);
-      // rescale O only when some row's running max moved (alpha == 1 exactly otherwise)
-      if (__ballot(alpha != 1.f) != 0) {
+    }
+    // rescale O only when some row's running max moved (alpha == 1 exactly otherwise)
+#pragma unroll
+    for (int T = 0; T < kPrefillTiles; ++T) {
+      if (__ballot(alpha[T] != 1.f) != 0) {
         float ar[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ar[r] = lane_from(alpha, 4 * grp + r);
+        for (int r = 0; r < 4; ++r) ar[r] = lane_from(alpha[T], 4 * grp + r);
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) {
 #pragma unroll

@@ -215,3 +215,25 @@ def test_work_order_ties_empty_chunks_and_many_sequences(num_seqs, context, chun
     got = _out_f64(pre.out, "fp16")
     assert np.isfinite(got).all()
     assert np.abs(got - ref).max() <= TOL["fp16"]
+
+
+@pytest.mark.parametrize("dtype,g", [("fp16", 1), ("bf16", 4)])
+def test_negative_scale(dtype, g):
+    """A negative softmax scale (the kernel carries it by negating the queries,
+    so the per-step row maximum stays a maximum of the scores)."""
+    import math
+
+    wl = synth.make_prefill_workload(8800 + g, num_seqs=4, num_heads=2 * g, num_kv_heads=2, dtype=dtype,
+                                     context=(40, 400), chunk=(1, 130))
+
+    class _NegativeScale(type(wl)):
+        @property
+        def scale(self):
+            return -1.0 / math.sqrt(128)
+
+    wl.__class__ = _NegativeScale
+    pre = harness.build_prefill(wl)
+    _, _, _, ref = opre.run_prefill(wl)
+    got = _out_f64(pre.out, dtype)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= TOL[dtype]
