@@ -36,8 +36,8 @@ namespace pkv {
 // ---------------------------------------------------------------------------
 
 // Step geometry, measured on MI355X over both prefill batches and the
-// prefix-cached admission: 2-block steps with 3 buffers (48 KiB of LDS, 163
-// VGPRs, so 3 work-groups per compute unit) against 2 per unit with 4 buffers:
+// prefix-cached admission: 2-block steps with 3 buffers (48 KiB of LDS, at
+// most 168 VGPRs, so 3 work-groups per compute unit) against 2 per unit with 4 buffers:
 // 7%, 13% and 19% shorter calls; 1-block steps or 4-block steps, 4 tiles per
 // wave (1 work-group per unit) and 1 tile per wave (4 per unit) were slower.
 constexpr int kStageBlocks = 2;  // blocks per LDS step
