@@ -43,6 +43,9 @@ namespace pkv {
 constexpr int kStageBlocks = 2;  // blocks per LDS step
 constexpr int kStageBufs = 3;    // LDS step buffers: up to kStageBufs - 1 steps in flight
 constexpr int kPrefillGroupsPerCu = 3;
+// Lazy softmax reference of the mask-free update: 2^8 bounds P well inside the
+// 16-bit range of its operand (fp16 max 65504).
+constexpr float kLazyShift = 8.f;
 
 // Blocks that the work-group holding chunk query qi streams: up to the block
 // of its last query's position.  Shared by the prefill kernel and its reduce.
@@ -374,8 +377,13 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
       for (int T = 0; T < kPrefillTiles; ++T) e[T] = cross_row_max(e[T]);
 #pragma unroll
       for (int T = 0; T < kPrefillTiles; ++T) {
-        const float m_new = fmaxf(m[T], e[T] * sc);
-        alpha[T] = exp2_fast(m[T] - m_new);
+        // the reference moves only when the row maximum passes it by more than
+        // kLazyShift (log2 units), so P = 2^(x - m) stays below 2^kLazyShift and
+        // O is rescaled rarely; O, z and m keep the same meaning
+        const float m_cand = e[T] * sc;
+        const bool move = m_cand > m[T] + kLazyShift;
+        const float m_new = move ? m_cand : m[T];
+        alpha[T] = move ? exp2_fast(m[T] - m_cand) : 1.f;
         const float neg = -m_new;
         float zs = 0.f;
 #pragma unroll
