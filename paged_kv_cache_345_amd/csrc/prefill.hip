@@ -362,8 +362,12 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
     uint2 P[kPrefillTiles][kStageBlocks];
     float alpha[kPrefillTiles];
     if (kFast) {
-      // row maxima of the raw scores of both tiles first (sc >= 0: the max of
-      // S sc is sc times the max of S), in one stretch of code
+      // Lazy reference: a row's m moves only when the row maximum of the step
+      // passes it by more than kLazyShift (log2 units), so P = 2^(x - m) stays
+      // below 2^kLazyShift and O is rescaled rarely; O, z and m keep their
+      // meaning.  Each lane first tests its own 8 scores (sc >= 0: the max of
+      // S sc is sc times the max of S); only when some lane of the wave passes
+      // is the row maximum reduced across the 4 rows and the reference moved.
       float e[kPrefillTiles];
 #pragma unroll
       for (int T = 0; T < kPrefillTiles; ++T) {
@@ -374,17 +378,15 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
           for (int r = 0; r < 4; ++r) e[T] = fmaxf(e[T], S[T][b][r]);
       }
 #pragma unroll
-      for (int T = 0; T < kPrefillTiles; ++T) e[T] = cross_row_max(e[T]);
-#pragma unroll
       for (int T = 0; T < kPrefillTiles; ++T) {
-        // the reference moves only when the row maximum passes it by more than
-        // kLazyShift (log2 units), so P = 2^(x - m) stays below 2^kLazyShift and
-        // O is rescaled rarely; O, z and m keep the same meaning
-        const float m_cand = e[T] * sc;
-        const bool move = m_cand > m[T] + kLazyShift;
-        const float m_new = move ? m_cand : m[T];
-        alpha[T] = move ? exp2_fast(m[T] - m_cand) : 1.f;
-        const float neg = -m_new;
+        alpha[T] = 1.f;
+        if (__ballot(e[T] * sc > m[T] + kLazyShift) != 0) {
+          const float mx = cross_row_max(e[T]) * sc;
+          const bool move = mx > m[T] + kLazyShift;
+          alpha[T] = move ? exp2_fast(m[T] - mx) : 1.f;
+          m[T] = move ? mx : m[T];
+        }
+        const float neg = -m[T];
         float zs = 0.f;
 #pragma unroll
         for (int b = 0; b < kStageBlocks; ++b) {
@@ -393,7 +395,6 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
           zs = DT::dot2(P[T][b].x, ones, zs);
           zs = DT::dot2(P[T][b].y, ones, zs);
         }
-        m[T] = m_new;
         z[T] = fmaf(z[T], alpha[T], zs);
       }
     } else {
