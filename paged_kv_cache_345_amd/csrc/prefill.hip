@@ -377,15 +377,23 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
 #pragma unroll
           for (int r = 0; r < 4; ++r) e[T] = fmaxf(e[T], S[T][b][r]);
       }
+      bool pass = false;
 #pragma unroll
       for (int T = 0; T < kPrefillTiles; ++T) {
         alpha[T] = 1.f;
-        if (__ballot(e[T] * sc > m[T] + kLazyShift) != 0) {
+        pass |= e[T] * sc > m[T] + kLazyShift;
+      }
+      if (__ballot(pass) != 0) {  // rare: one branch for both tiles keeps the common path straight
+#pragma unroll
+        for (int T = 0; T < kPrefillTiles; ++T) {
           const float mx = cross_row_max(e[T]) * sc;
           const bool move = mx > m[T] + kLazyShift;
           alpha[T] = move ? exp2_fast(m[T] - mx) : 1.f;
           m[T] = move ? mx : m[T];
         }
+      }
+#pragma unroll
+      for (int T = 0; T < kPrefillTiles; ++T) {
         const float neg = -m[T];
         float zs = 0.f;
 #pragma unroll
