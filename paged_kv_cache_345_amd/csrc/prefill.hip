@@ -361,6 +361,20 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
 
     uint2 P[kPrefillTiles][kStageBlocks];
     float alpha[kPrefillTiles];
+    // O[T] *= alpha of its rows when some row's reference moved (alpha == 1
+    // exactly otherwise); the alpha of row c sits in lane c, and lane (grp, col)
+    // holds rows 4 grp .. 4 grp + 3
+    auto rescale = [&](int T) __attribute__((always_inline)) {
+      if (__ballot(alpha[T] != 1.f) == 0) return;
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = lane_from(alpha[T], 4 * grp + r);
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[T][jd][r] *= ar[r];
+      }
+    };
     if (kFast) {
       // Lazy reference: a row's m moves only when the row maximum of the step
       // passes it by more than kLazyShift (log2 units), so P = 2^(x - m) stays
@@ -390,6 +404,7 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
           const bool move = mx > m[T] + kLazyShift;
           alpha[T] = move ? exp2_fast(m[T] - mx) : 1.f;
           m[T] = move ? mx : m[T];
+          rescale(T);
         }
       }
 #pragma unroll
@@ -434,19 +449,9 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
         z[T] = fmaf(z[T], alpha[T], zs);
       }
     }
-    // rescale O only when some row's running max moved (alpha == 1 exactly otherwise)
+    if (!kFast) {
 #pragma unroll
-    for (int T = 0; T < kPrefillTiles; ++T) {
-      if (__ballot(alpha[T] != 1.f) != 0) {
-        float ar[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ar[r] = lane_from(alpha[T], 4 * grp + r);
-#pragma unroll
-        for (int jd = 0; jd < 8; ++jd) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[T][jd][r] *= ar[r];
-        }
-      }
+      for (int T = 0; T < kPrefillTiles; ++T) rescale(T);
     }
 
     // O += P V over both blocks of the step in one 16x16x32 product per
