@@ -503,6 +503,12 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
   };
 
   const int nsteps = (nb + kStageBlocks - 1) / kStageBlocks;
+  // The mask-free steps form a prefix of the segment: step st is one exactly
+  // when its kStageBlocks blocks all lie in the segment and below the wave's
+  // first position, j0 + (st + 1) kStageBlocks <= (lo_pos + 1) / 16 (which
+  // also puts them below its last one).  Counted once.
+  const int fast_steps =
+      hi_pos < 0 ? 0 : min(nb / kStageBlocks, max(0, (min(lo_pos, 0x7ffffff0) + 1) / kBlockSize - j0) / kStageBlocks);
   for (int st = 0; st < min(nsteps, kStageBufs - 1); ++st) issue(st);
   wait_steps(min(nsteps, kStageBufs - 1) - 1);
   step_barrier();
@@ -511,17 +517,16 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
     // the buffer of step st + kStageBufs - 1 was last read in step st - 1, before the barrier that ended it
     if (st + kStageBufs - 1 < nsteps) issue(st + kStageBufs - 1);
 
-    // live blocks of the step for this wave: a prefix (the step's blocks inside
-    // the segment, up to the wave's last position); the fast path takes steps
-    // whose 4 blocks are live and visible to every valid row of the wave
     const int jstep = j0 + st * kStageBlocks;
-    const int nlive =
-        hi_pos < 0 ? 0 : max(0, min(min(kStageBlocks, nb - st * kStageBlocks), hi_pos / kBlockSize - jstep + 1));
-    const bool fast = nlive == kStageBlocks && (jstep + kStageBlocks) * kBlockSize - 1 <= lo_pos;
-    if (fast)
+    if (st < fast_steps) {
       step.template operator()<true>(buf, jstep, kStageBlocks);
-    else if (nlive > 0)
-      step.template operator()<false>(buf, jstep, nlive);
+    } else {
+      // live blocks of the step for this wave: a prefix (the step's blocks
+      // inside the segment, up to the wave's last position)
+      const int nlive =
+          hi_pos < 0 ? 0 : max(0, min(min(kStageBlocks, nb - st * kStageBlocks), hi_pos / kBlockSize - jstep + 1));
+      if (nlive > 0) step.template operator()<false>(buf, jstep, nlive);
+    }
 
     if (st + 1 < nsteps) {
       // step st + 1 landed; the steps after it that were issued may stay in flight
