@@ -18,8 +18,9 @@ namespace pkv {
 // every wave reads its fragments from there for both of its tiles.  Per step
 // and tile: S = K Q^T (16x16x32 products), one online-softmax update over the
 // step's keys (the causal mask by row position is evaluated only in steps
-// that reach past some row's position), then O += P V (16x16x32 products over
-// the step's two blocks).
+// that reach past some row's position; the other steps keep a lazy softmax
+// reference that moves only when a score passes it by 2^8), then O += P V
+// (16x16x32 products over the step's two blocks).
 // A block wholly past every position of a wave is skipped by that wave.  Each
 // wave writes its own rows.
 //
