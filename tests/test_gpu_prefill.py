@@ -201,16 +201,19 @@ def _ref_rows_at(wl, s, rows, heads):
     return out
 
 
-@pytest.mark.parametrize("num_seqs,context,chunk", [(256, (16, 18), (0, 6)), (300, (1, 60), (1, 9))])
-def test_work_order_ties_empty_chunks_and_many_sequences(num_seqs, context, chunk):
+@pytest.mark.parametrize("num_seqs,context,chunk,pt", [(256, (16, 18), (0, 6), 0), (300, (1, 60), (1, 9), 0),
+                                                  (256, (40, 90), (0, 40), 16), (300, (40, 90), (1, 40), 16)])
+def test_work_order_ties_empty_chunks_and_many_sequences(num_seqs, context, chunk, pt):
     """Up to 256 sequences the work-groups take their items longest sequence
     first, from a rank every work-group computes: with block counts tied
     across most sequences and some chunks empty, every (sequence, unit) must
-    still be evaluated exactly once.  Past 256 sequences the plain order runs."""
-    wl = synth.make_prefill_workload(8600 + num_seqs, num_seqs=num_seqs, num_heads=4, num_kv_heads=2, dtype="fp16",
-                                     context=context, chunk=chunk)
+    still be evaluated exactly once.  Past 256 sequences the plain order runs.
+    With 16-token segments every item is also split across several segments
+    and merged by the reduce kernel, in both orders."""
+    wl = synth.make_prefill_workload(8600 + num_seqs + pt, num_seqs=num_seqs, num_heads=4, num_kv_heads=2,
+                                     dtype="fp16", context=context, chunk=chunk)
     assert (wl.chunk_lens == 0).any() == (chunk[0] == 0)
-    pre = harness.build_prefill(wl)
+    pre = harness.build_prefill(wl, partition_tokens=pt)
     _, _, _, ref = opre.run_prefill(wl)
     got = _out_f64(pre.out, "fp16")
     assert np.isfinite(got).all()
