@@ -3,6 +3,10 @@
 fp16 values are numpy float16 arrays.  bf16 values are uint16 bit patterns: a
 bfloat16 is the upper half of a float32, so shifting the bits left by 16 and
 reinterpreting as float32 is exact.
+
+Test infrastructure only.  Pinned in tests/test_oracle_numerics.py against
+torch's own float16/bfloat16 conversions on all 65,536 bit patterns and
+against closed forms of the two formats (a shift by 15 instead of 16 fails).
 """
 
 import numpy as np
