@@ -18,7 +18,9 @@ formula for a chunk's attention; the plainest reading, taken here:
 Pins (``tests/test_oracle_prefill.py``): a chunk of one token is decode
 attention; the whole prompt as one chunk equals textbook causal attention in
 explicit loops; the first position returns its own V row; splitting a chunk in
-two changes nothing.
+two changes nothing.  ``causal_chunk_ref`` (the same definition with the scores
+of a block of queries taken as one matrix product) equals ``prefill_ref`` and
+the explicit-loop brute force, and a causal bound one key too wide fails it.
 """
 
 from __future__ import annotations
@@ -75,3 +77,38 @@ def run_prefill(wl, *, compute_out: bool = True, seqs: Sequence[int] = None):
         out = prefill_ref(wl.q, kc, vc, tables, wl.context_lens, wl.query_start, wl.scale, wl.num_kv_heads,
                           wl.dtype, seqs=seqs)
     return kc, vc, tables, out
+
+
+def causal_chunk_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, first_pos: int,
+                     row_block: int = 128) -> np.ndarray:
+    """Every query of one sequence's chunk, by matrix products.
+
+    q: float64 [C, Hq, D], chunk query j at absolute position first_pos + j;
+    k, v: float64 [L, Hkv, D] with L >= first_pos + C (the sequence's rows in
+    logical order).  The same definition as ``prefill_ref``: for each KV head,
+    the scores of its query heads against the keys are one product over a
+    block of queries, keys past a query's position get weight zero (the causal
+    bound), then the softmax with its maximum shift and the weighted sum of V
+    rows.  Returns float64 [C, Hq, D].
+    """
+    C, hq, d = q.shape
+    L, hkv, _ = k.shape
+    g = hq // hkv
+    assert first_pos >= 0 and first_pos + C <= L
+    pos = first_pos + np.arange(C)
+    out = np.empty((C, hq, d), dtype=np.float64)
+    for j in range(hkv):
+        kj = np.ascontiguousarray(k[:, j, :])
+        vj = np.ascontiguousarray(v[:, j, :])
+        heads = slice(j * g, (j + 1) * g)
+        for r0 in range(0, C, row_block):
+            r1 = min(C, r0 + row_block)
+            n = int(pos[r1 - 1]) + 1  # keys any row of this block can see
+            qq = q[r0:r1, heads, :]  # [R, g, D]
+            logits = scale * (qq.reshape(-1, d) @ kj[:n].T).reshape(r1 - r0, g, n)
+            visible = np.arange(n)[None, None, :] <= pos[r0:r1, None, None]
+            logits = np.where(visible, logits, -np.inf)
+            m = logits.max(axis=-1, keepdims=True)
+            w = np.exp(logits - m)  # exactly 0 past the position
+            out[r0:r1, heads] = (w @ vj[:n]) / w.sum(axis=-1, keepdims=True)
+    return out

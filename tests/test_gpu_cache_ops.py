@@ -4,10 +4,12 @@ copy, gather): bit-exact against the oracle.  Marked gpu."""
 import numpy as np
 import pytest
 
+import fullsize
 import harness
 import oracle
 import synth
 from layout import decode_pages, encode_pages
+from oracle import fp8 as ofp8
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -98,26 +100,57 @@ def test_copy_blocks_and_padding_slots():
     assert np.array_equal(decode_pages(harness.to_host_bits(vc), "v"), ov)
 
 
-def test_full_size_llama13b_step_sampled():
-    """LLaMA-13B-shaped batch at full size: the copy-on-write pairs, and the
-    gathered K/V of sampled sequences (every group member among them) equal the
-    generator's values bit for bit."""
-    wl = synth.make_workload("llama13b")
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama7b", "llama13b"])
+def test_full_size_step_caches_bit_exact(name):
+    """The LLaMA-shaped batches at full size, in the configuration the bench
+    times: both whole caches after the decode step (every prior token, the
+    copy-on-write copies, the new tokens, and garbage everywhere else), the
+    slot mapping, the copy pairs and the block tables, bit for bit against the
+    oracle's step from the same garbage."""
+    wl = synth.make_workload(name)
+    step = _full_cache_check(wl)
+    if name == "llama13b":
+        assert step.block_pairs_host.shape == (22, 2)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["gqa", "long", "llama13b_fp8", "gqa_fp8"])
+def test_full_size_live_rows_bit_exact(name):
+    """The other full-size batches: every live row of every sequence, read
+    back through its block table with gather_cache, equals the generator's
+    value (16-bit) or the oracle's E4M3 code of it (fp8), bit for bit."""
+    wl = synth.make_workload(name)
     step = harness.build_step(wl)
-    assert step.block_pairs_host.shape == (22, 2)
-    sample = sorted(set([0, 1, 2, 3, 4, 5, 37, 38, 39, 64, 127] + [int(np.argmax(wl.context_lens))]))
-    lens = wl.context_lens[sample].astype(np.int32)
-    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
-    ko = torch.empty((int(lens.sum()), 40, 128), dtype=torch.float16, device="cuda")
-    vo = torch.empty_like(ko)
-    idx = torch.tensor(sample, device="cuda")
-    pkv.gather_cache(ko, vo, step.k_cache, step.v_cache, step.block_tables[idx].contiguous(),
-                     step.context_lens[idx].contiguous(), torch.from_numpy(offs).cuda())
-    kh, vh = harness.to_host_bits(ko), harness.to_host_bits(vo)
-    for i, s in enumerate(sample):
-        k, v = wl.seq_kv(s)
-        assert np.array_equal(kh[offs[i]:offs[i] + lens[i]], k.view(np.uint16)), s
-        assert np.array_equal(vh[offs[i]:offs[i] + lens[i]], v.view(np.uint16)), s
+    fp8 = wl.kv_dtype == "fp8e4m3"
+    cdt = torch.uint8 if fp8 else harness.torch_dtype(wl.dtype)
+    hkv = wl.num_kv_heads
+    for lo in range(0, wl.num_seqs, 32):
+        seqs = list(range(lo, min(lo + 32, wl.num_seqs)))
+        lens = wl.context_lens[seqs].astype(np.int32)
+        offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+        ko = torch.empty((int(lens.sum()), hkv, 128), dtype=cdt, device="cuda")
+        vo = torch.empty_like(ko)
+        idx = torch.tensor(seqs, device="cuda")
+        pkv.gather_cache(ko, vo, step.k_cache, step.v_cache, step.block_tables[idx].contiguous(),
+                         step.context_lens[idx].contiguous(), torch.from_numpy(offs).cuda())
+        if fp8:
+            kh, vh = ko.cpu().numpy(), vo.cpu().numpy()
+        else:
+            kh, vh = harness.to_host_bits(ko), harness.to_host_bits(vo)
+
+        def one(i):
+            k, v = wl.seq_kv(seqs[i])
+            if fp8:
+                k = ofp8.quantize_ref(k, wl.dtype, wl.k_scale)
+                v = ofp8.quantize_ref(v, wl.dtype, wl.v_scale)
+            else:
+                k, v = k.view(np.uint16), v.view(np.uint16)
+            a, b = offs[i], offs[i] + lens[i]
+            return bool(np.array_equal(kh[a:b], k) and np.array_equal(vh[a:b], v))
+
+        ok = fullsize.host_map(one, range(len(seqs)))
+        assert all(ok), [seqs[i] for i, o in enumerate(ok) if not o]
 
 
 def test_validate_mode_catches_contract_violations(monkeypatch):

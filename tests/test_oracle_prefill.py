@@ -81,3 +81,39 @@ def test_planted_off_by_one_fails():
     for p in range(L - 1):
         assert not np.allclose(bad[p], good[p])
     assert np.array_equal(bad[-1], good[-1])
+
+
+@pytest.mark.parametrize("seed,g,dtype", [(11, 1, "fp16"), (12, 4, "bf16"), (13, 3, "fp16")])
+def test_causal_chunk_ref_equals_prefill_ref(seed, g, dtype):
+    """The by-products form of the chunk attention gives the per-query rows of
+    prefill_ref, for chunks that start mid-context and whole prompts, with
+    query blocks smaller than the chunk."""
+    wl = synth.make_prefill_workload(seed, num_seqs=4, num_heads=2 * g, num_kv_heads=2, dtype=dtype,
+                                     context=(1, 150), chunk=(1, 120))
+    _, _, _, out = prefill.run_prefill(wl)
+    qs = wl.query_start
+    for s in range(wl.num_seqs):
+        k, v = wl.seq_kv(s)
+        L, C = int(wl.context_lens[s]), int(wl.chunk_lens[s])
+        q = oracle.to_f64(wl.q[qs[s]:qs[s] + C], dtype)
+        got = prefill.causal_chunk_ref(q, oracle.to_f64(k, dtype), oracle.to_f64(v, dtype), wl.scale, L - C,
+                                       row_block=16)
+        np.testing.assert_allclose(got, out[qs[s]:qs[s] + C], rtol=0, atol=1e-12)
+
+
+def test_causal_chunk_ref_brute_force_and_planted_bound():
+    """Against textbook attention in explicit loops on a whole prompt; a mask
+    one key too wide (keys 0..p+1) fails."""
+    wl = synth.make_prefill_workload(14, num_seqs=1, num_heads=4, num_kv_heads=2, dtype="bf16",
+                                     context=(21, 21), chunk=(21, 21))
+    k, v = wl.seq_kv(0)
+    kf, vf = oracle.to_f64(k, "bf16"), oracle.to_f64(v, "bf16")
+    q = oracle.to_f64(wl.q, "bf16")
+    got = prefill.causal_chunk_ref(q, kf, vf, wl.scale, 0, row_block=8)
+    for p in range(21):
+        ref = oracle.brute_force_ref(q[p].tolist(), kf[:p + 1].tolist(), vf[:p + 1].tolist(), wl.scale)
+        np.testing.assert_allclose(got[p], np.array(ref), rtol=0, atol=1e-12)
+    # planted: every query sees one key more (the last row has none to add)
+    wide = np.stack([prefill.causal_chunk_ref(q[p:p + 1], kf, vf, wl.scale, min(p + 1, 20))[0] for p in range(21)])
+    for p in range(20):
+        assert not np.allclose(wide[p], got[p])
