@@ -147,6 +147,29 @@ pkv_status paged_attn_decode_run(void* out, const void* q, const void* k_cache, 
                                  const pkv_cache_desc* cache, int32_t partition_tokens,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* paged_attn_decode_noalloc — for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same call as paged_attn_decode without the workspace
+ * arguments.  The work list and the segment partials live in a scratch array
+ * inside the library, PKV_NOALLOC_SCRATCH_BYTES per GPU, reserved on every GPU
+ * the library is loaded on and held until the process ends; its address is
+ * looked up once per device on the first call made with that device current.
+ * No hipMalloc/hipFree or other allocation happens in the call.
+ *   - PKV_ERR_INVALID when paged_attn_decode_workspace_size() of these
+ *     arguments exceeds PKV_NOALLOC_SCRATCH_BYTES (use paged_attn_decode with
+ *     a caller workspace then), besides paged_attn_decode's own errors;
+ *   - PKV_ERR_DEVICE if the scratch address cannot be obtained.
+ * Every call on one GPU shares that GPU's scratch, and the run reads what the
+ * call's own plan wrote there: calls that overlap on one GPU (two streams,
+ * or two host threads) race and must be serialised by the caller.  Nothing in
+ * the scratch has to start at any value. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pkv_status paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     float scale, int32_t num_kv_heads,
+                                     int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                     const pkv_cache_desc* cache, int32_t partition_tokens, void* stream);
+
 /* Workspace bytes paged_attn_decode needs for these arguments: the work list
  * (up to 4096 sequences) and, when a sequence can span several segments, the
  * fp32 segment partials.  (size_t)-1 for invalid arguments. */

@@ -42,6 +42,7 @@ PKV_ERR_OUT_OF_BLOCKS = 4
 PKV_F16 = 0
 PKV_BF16 = 1
 PKV_FP8_E4M3 = 2
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES: the scratch of paged_attn_decode_noalloc
 
 # Every symbol pagedkv.h declares, with (restype, argtypes).
 _i32 = ctypes.c_int32
@@ -71,6 +72,8 @@ SIGNATURES = {
     "paged_attn_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _i32,
                                  _vp, _sz, _vp]),
     "paged_attn_decode_plan": (_i32, [_vp, _i32, _i32, _i32, _DP, _i32, _vp, _sz, _vp]),
+    "paged_attn_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _i32,
+                                         _vp]),
     "paged_attn_decode_run": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _i32,
                                      _vp, _sz, _vp]),
     "paged_attn_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _DP]),
@@ -302,6 +305,40 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
                                  ctypes.byref(desc), int(partition_tokens), ws_ptr, ws_bytes,
                                  _stream_handle(stream))
     _check(st, "paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                              num_kv_heads: int, *, partition_tokens: int = 0, stream=None):
+    """paged_attn_decode with the library's per-GPU scratch as its workspace:
+    nothing is allocated, here or in the library.  Calls that overlap on one
+    GPU share that scratch and race; serialise them."""
+    torch = _torch()
+    desc = _desc_of(k_cache)
+    cache_dtype = torch.uint8 if desc.dtype == PKV_FP8_E4M3 else q.dtype
+    if desc.num_kv_heads != num_kv_heads:
+        raise ValueError("num_kv_heads does not match the cache")
+    num_seqs, num_heads, hs = q.shape
+    if hs != HEAD_SIZE or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must be [num_seqs, num_heads, 128]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    mbps = int(block_tables.shape[1])
+    ptrs = [_gpu(out, "out", q.dtype, 3), _gpu(q, "q", None, 3), _gpu(k_cache, "k_cache", cache_dtype),
+            _gpu(v_cache, "v_cache", cache_dtype), _gpu(block_tables, "block_tables", torch.int32, 2),
+            _gpu(context_lens, "context_lens", torch.int32, 1)]
+    if context_lens.shape[0] != num_seqs or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("context_lens / v_cache shape mismatch")
+    if num_seqs:
+        need = workspace_size(num_seqs, num_heads, mbps, desc, partition_tokens)
+        if need > NOALLOC_SCRATCH_BYTES:
+            raise ValueError(f"paged_attn_decode_noalloc: this batch needs a {need}-byte workspace, more than the "
+                             f"library's {NOALLOC_SCRATCH_BYTES}-byte scratch; call paged_attn_decode with a workspace")
+    if _validate.enabled():
+        _validate.check_tables(block_tables, context_lens, desc.num_blocks)
+    st = lib().paged_attn_decode_noalloc(*ptrs, float(scale), int(num_kv_heads), int(num_seqs), int(num_heads), mbps,
+                                         ctypes.byref(desc), int(partition_tokens), _stream_handle(stream))
+    _check(st, "paged_attn_decode_noalloc")
     return out
 
 

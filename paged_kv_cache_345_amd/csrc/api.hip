@@ -5,7 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "pagedkv.h"
 #include "pkv_device.h"
@@ -290,6 +292,61 @@ pkv_status paged_attn_decode_run_fp8(void* out, const void* q, const void* k_cac
   return decode_impl(false, out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, num_seqs,
                      num_heads, max_blocks_per_seq, cache, scales, partition_tokens, workspace, workspace_bytes,
                      stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of paged_attn_decode_noalloc: one copy per GPU (the code object's
+// device globals are placed on every device the library is loaded on).  Host
+// code never uses the array's name as an address: the device address comes
+// from hipGetSymbolAddress, once per device, and is kept per device below.
+static_assert(PKV_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch address on the current device, looked up on the first call.
+pkv_status scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKV_ERR_DEVICE;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                     int32_t num_kv_heads, int32_t num_seqs, int32_t num_heads,
+                                     int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                     int32_t partition_tokens, void* stream) {
+  DecodeLayout L;
+  pkv_status st = decode_layout(num_seqs, num_heads, max_blocks_per_seq, partition_tokens, cache, &L);
+  if (st != PKV_OK) return st;
+  if (L.total > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_INVALID;
+  void* ws = nullptr;
+  if (num_seqs > 0 && L.total > 0) {
+    st = scratch_on_current_device(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return decode_impl(true, out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, num_seqs,
+                     num_heads, max_blocks_per_seq, cache, nullptr, partition_tokens, ws,
+                     ws ? PKV_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 pkv_status paged_attn_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
