@@ -105,68 +105,158 @@ def measured_traffic(workload: str):
     return int(fields["traffic_bytes_per_call"])
 
 
-def cpu_baseline(wl, seconds: float):
-    """The fp64 oracle's paged decode on the host cores.  Setup and data
-    generation are untimed.  A third of the budget runs it on one thread
-    (whole passes over the batch, or a prefix of its sequences if one pass
-    alone exceeds the budget); the rest runs the same per-sequence calls on a
-    pool of one thread per host CPU (NumPy releases the interpreter lock in
-    its array work), and that all-core rate is the reported value."""
-    from concurrent.futures import ThreadPoolExecutor
+def host_cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (the machine type if absent)."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
+# --- cpu baseline: the oracle, in a child process that never touches the GPU ---
+
+_CB = {}  # the child's oracle state, inherited by its forked workers
+
+
+def _cb_eval(s):
+    """One sequence through the oracle's paged decode (a worker task):
+    (sequence, per-sequence KV bytes, max-abs error against the GPU output or
+    -1, CPU seconds)."""
+    import numpy as np
 
     import oracle
 
-    log("cpu baseline: building the oracle's cache (untimed)")
-    ref = oracle.run_decode_step(wl, compute_out=False)
-    per_token = 2 * wl.num_kv_heads * 128 * 2
-
-    def one(s):
-        if wl.kv_dtype == "fp8e4m3":
-            oracle.fp8.paged_decode_fp8_ref(wl.q, ref.k_cache, ref.v_cache, ref.block_tables, ref.context_lens,
+    wl, ref, got = _CB["wl"], _CB["ref"], _CB["got"]
+    c0 = time.process_time()
+    if wl.kv_dtype == "fp8e4m3":
+        o = oracle.fp8.paged_decode_fp8_ref(wl.q, ref.k_cache, ref.v_cache, ref.block_tables, ref.context_lens,
                                             wl.scale, wl.num_kv_heads, wl.dtype, wl.k_scale, wl.v_scale, seqs=[s])
-        else:
-            oracle.paged_decode_ref(wl.q, ref.k_cache, ref.v_cache, ref.block_tables, ref.context_lens,
+    else:
+        o = oracle.paged_decode_ref(wl.q, ref.k_cache, ref.v_cache, ref.block_tables, ref.context_lens,
                                     wl.scale, wl.num_kv_heads, wl.dtype, seqs=[s])
-        return int(wl.context_lens[s]) * per_token
+    err = -1.0 if got is None else float(np.abs(got[s] - o[0]).max())
+    per_token = 2 * wl.num_kv_heads * 128 * (1 if wl.kv_dtype == "fp8e4m3" else 2)
+    return s, int(wl.context_lens[s]) * per_token, err, time.process_time() - c0
 
-    # one thread
+
+def cpu_baseline_child(workload: str, seconds: float, decode_bytes: int, got_path: str) -> dict:
+    """The fp64 oracle's paged decode on the host cores, run in a process that
+    has not initialised the GPU, so its worker processes can be forked.  Setup
+    and data generation are untimed.  A third of the budget runs it on one
+    core (whole sequences, cycling through the batch); the rest runs the same
+    per-sequence calls on a pool of one worker process per host CPU (BLAS held
+    to one thread per worker), in three equal windows whose median rate is
+    reported.  Rates count the step's algorithmic decode bytes (every unique
+    live slot once, as for the GPU figure) per pass over the batch; the
+    per-sequence count is reported beside it.  Every row the baseline
+    evaluates is also compared with the GPU's timed output: max_abs_err."""
+    import multiprocessing as mp
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+
+    wl = synth.make_workload(workload)
+    log("cpu baseline: building the oracle's cache (untimed)")
+    _CB["wl"] = wl
+    _CB["ref"] = oracle.run_decode_step(wl, compute_out=False)
+    _CB["got"] = np.load(got_path) if got_path else None
+    S = wl.num_seqs
+    worst = [0.0, -1]
+    seen = set()
+
+    def note(r):
+        s, _b, e, _c = r
+        seen.add(s)
+        if e > worst[0]:
+            worst[0], worst[1] = e, s
+
+    threadpool_limits(limits=1, user_api="blas")  # also inherited by the forked workers
     budget1 = seconds / 3
-    nbytes1, wall1, seqs1 = 0, 0.0, 0
+    n1, b1, wall1 = 0, 0, 0.0
     while wall1 < budget1:
-        for s in range(wl.num_seqs):
-            t0 = time.perf_counter()
-            nbytes1 += one(s)
-            wall1 += time.perf_counter() - t0
-            seqs1 += 1
-            if wall1 >= budget1:
-                break
-    # one thread per host CPU: rounds of one sequence per thread, cycling
-    # through the batch, until the rest of the budget is used
-    threads = len(os.sched_getaffinity(0))
-    nbytes, seqs, nxt = 0, 0, 0
-    t0, c0 = time.perf_counter(), time.process_time()
-    with ThreadPoolExecutor(threads) as pool:
-        while time.perf_counter() - t0 < seconds - budget1:
-            batch = [(nxt + i) % wl.num_seqs for i in range(threads)]
-            nxt = (nxt + threads) % wl.num_seqs
-            nbytes += sum(pool.map(one, batch))
-            seqs += threads
-    wall, cpu = time.perf_counter() - t0, time.process_time() - c0
+        t0 = time.perf_counter()
+        r = _cb_eval(n1 % S)
+        wall1 += time.perf_counter() - t0
+        note(r)
+        b1 += r[1]
+        n1 += 1
+    workers = len(os.sched_getaffinity(0))
+    window = (seconds - budget1) / 3
+    rates, nxt, evals, cpu = [], n1, 0, 0.0
+    with mp.get_context("fork").Pool(workers) as pool:
+        pool.map(_cb_eval, range(min(S, workers)))  # start-up of the workers, untimed
+        t_all = time.perf_counter()
+        for _ in range(3):
+            # keep two tasks per worker in flight until the window ends, then drain
+            n0, b0, t0 = 0, 0, time.perf_counter()
+            pending = []
+            while pending or time.perf_counter() - t0 < window:
+                while len(pending) < 2 * workers and time.perf_counter() - t0 < window:
+                    pending.append(pool.apply_async(_cb_eval, ((nxt % S),)))
+                    nxt += 1
+                r = pending.pop(0).get()
+                note(r)
+                b0 += r[1]
+                cpu += r[3]
+                n0 += 1
+            rates.append((n0, b0, time.perf_counter() - t0))
+            evals += n0
+    wall = time.perf_counter() - t_all
+    med = sorted(rates, key=lambda r: r[0] / r[2])[1]
+    gbs = lambda n, t: n / S * decode_bytes / t / 1e9  # noqa: E731
     return {
-        "value": round(nbytes / wall / 1e9, 4),
+        "value": round(gbs(med[0], med[2]), 4),
         "unit": "GB/s",
         "cores": max(1, int(round(cpu / wall))),
         "kind": "oracle",
-        "sample": (f"fp64 numpy paged decode (oracle paged decode reference), {seqs} sequence evaluations "
-                   f"= {seqs / wl.num_seqs:.2f} passes over the {wl.num_seqs}-sequence batch, all {wl.num_heads} "
-                   f"heads, on a pool of {threads} threads "
-                   f"({wall:.1f} s wall, {cpu:.1f} s CPU: cores = CPU / wall time); per-sequence KV bytes / wall time"),
-        "single_thread": {"value": round(nbytes1 / wall1 / 1e9, 4), "unit": "GB/s",
-                          "sample": f"{seqs1} sequence evaluations, {wall1:.1f} s"},
-        "threads": threads,
-        "host_cpus": threads,
-        "host_cpu_model": platform.processor() or platform.machine(),
+        "sample": (f"fp64 numpy paged decode (the oracle's paged decode reference) on whole sequences of the "
+                   f"batch, all {wl.num_heads} heads: {evals} sequence evaluations = {evals / S:.2f} passes over the "
+                   f"{S}-sequence batch on {workers} worker processes in 3 windows of {window:.1f} s "
+                   f"({wall:.1f} s wall, {cpu:.1f} s CPU in the workers; cores = CPU / wall time); value = the "
+                   f"median window's passes x the step's algorithmic decode bytes (unique live slots, as for the "
+                   f"GPU) / wall time"),
+        "per_sequence_bytes_value": round(med[1] / med[2] / 1e9, 4),
+        "window_rates_gbs": [round(gbs(r[0], r[2]), 4) for r in rates],
+        "single_thread": {"value": round(gbs(n1, wall1), 4), "unit": "GB/s",
+                          "per_sequence_bytes_value": round(b1 / wall1 / 1e9, 4),
+                          "sample": f"{n1} sequence evaluations on one core, {wall1:.1f} s"},
+        "workers": workers,
+        "host_cpus": workers,
+        "host_cpu_model": host_cpu_model(),
+        "max_abs_err": None if _CB["got"] is None else round(worst[0], 7),
+        "max_abs_err_sequence": None if _CB["got"] is None else worst[1],
+        "max_abs_err_rows": (None if _CB["got"] is None else
+                             f"every head of the {len(seen)} distinct sequences the baseline evaluated"),
     }
+
+
+def cpu_baseline(wl, seconds: float, nb, gpu_out=None):
+    """Runs ``cpu_baseline_child`` in a child Python process (this process has
+    initialised the GPU, and forking it is not safe); the GPU output goes to
+    the child through a temporary .npy file."""
+    import subprocess
+    import tempfile
+
+    import numpy as np
+
+    with tempfile.TemporaryDirectory() as tmp:
+        path = ""
+        if gpu_out is not None:
+            path = os.path.join(tmp, "gpu_out.npy")
+            np.save(path, gpu_out)
+        cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", wl.spec.name,
+               str(seconds), str(nb["decode"]), path]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError(f"cpu baseline child failed with status {r.returncode}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def copy_probe(mib: int, reps: int = 3):
@@ -214,8 +304,9 @@ def prefill_bench(args, name: str) -> int:
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / K
-    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    log(f"prefill call avg {call_ms * 1e3:.1f} us")
+    calls = np.array([a.elapsed_time(b) for a, b in ev])
+    call_ms = float(np.median(calls))
+    log(f"prefill call median {call_ms * 1e3:.1f} us, min {calls.min() * 1e3:.1f} us, mean {calls.mean() * 1e3:.1f} us")
     L = wl.context_lens.astype(np.int64)
     C = wl.chunk_lens.astype(np.int64)
     visible = int(sum(int(((L[s] - C[s] + 1) + L[s]) * C[s] // 2) for s in range(wl.num_seqs)))  # sum of p + 1
@@ -238,6 +329,9 @@ def prefill_bench(args, name: str) -> int:
         "flops": flops,
         "bytes": {"kv": kv_bytes, "q_out": qo_bytes},
         "prefill_call_us": round(call_ms * 1e3, 2),
+        "timing": {"flushed": False, "prefill_call_us": {"median": round(call_ms * 1e3, 2),
+                                                          "min": round(float(calls.min()) * 1e3, 2),
+                                                          "mean": round(float(calls.mean()) * 1e3, 2)}},
         "query_tokens_per_s": round(int(C.sum()) / (call_ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "kernel": "paged_attn_prefill: prefill_kernel", "achieved": round(tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
@@ -472,11 +566,20 @@ def main() -> int:
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-flush", dest="flush", action="store_false",
+                    help="decode workloads: run the timed steps back to back, without the cache flush")
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: also time the step captured in a HIP graph and replayed")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the bench, run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--cpu-baseline-child", nargs=4, metavar=("WORKLOAD", "SECONDS", "DECODE_BYTES", "GPU_OUT"),
+                    help=argparse.SUPPRESS)
     args = ap.parse_args()
+
+    if args.cpu_baseline_child:  # the cpu_baseline leg's child process: no GPU, no torch
+        w, sec, nbytes, path = args.cpu_baseline_child
+        print(json.dumps(cpu_baseline_child(w, float(sec), int(nbytes), path)), flush=True)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -514,36 +617,49 @@ def main() -> int:
     log(f"setup {time.perf_counter() - t0:.1f} s (partition {pkv.partition_tokens_for(wl.num_seqs, wl.num_heads, step.max_blocks, step.desc, step.partition_tokens)} tokens)")
     nb = step_bytes(wl, step)
 
-    for _ in range(args.warmup):
+    # Cache flush between timed steps, outside the timed events: write a 1 GiB
+    # scratch buffer, then read it back, so the 256 MB memory-side cache and
+    # the L2s hold only clean scratch lines when a step starts.
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.flush else None
+    sink = torch.empty(1, dtype=torch.int64, device="cuda")
+
+    def flush(i):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
+            torch.sum(scratch.view(torch.int64), dim=0, keepdim=True, out=sink)
+
+    def one_step():
         step.copy()
         step.write()
         step.plan()
+
+    for i in range(args.warmup):
+        flush(i)
+        one_step()
         step.run()
     torch.cuda.synchronize()
 
     K = args.steps
-    dec_start = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    dec_end = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    all_start = torch.cuda.Event(enable_timing=True)
-    all_end = torch.cuda.Event(enable_timing=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    all_start.record()
     for i in range(K):
-        step.copy()
-        step.write()
-        step.plan()
-        dec_start[i].record()
+        flush(i)
+        e0, e1, e2 = ev[i]
+        e0.record()
+        one_step()
+        e1.record()
         step.run()
-        dec_end[i].record()
-    all_end.record()
+        e2.record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - w0
-    ms_per_step = all_start.elapsed_time(all_end) / K
-    dec_ms = [a.elapsed_time(b) for a, b in zip(dec_start, dec_end)]
-    dec_avg = float(np.mean(dec_ms))
-    log(f"step {ms_per_step * 1e3:.1f} us (wall {wall_s / K * 1e6:.1f} us); decode avg {dec_avg * 1e3:.1f} us, "
-        f"min {min(dec_ms) * 1e3:.1f} us")
+    step_ms = np.array([a.elapsed_time(c) for a, _b, c in ev])
+    dec_ms = np.array([b.elapsed_time(c) for _a, b, c in ev])
+    ms_per_step = float(step_ms.mean())
+    dec_med, dec_min, dec_avg = float(np.median(dec_ms)), float(dec_ms.min()), float(dec_ms.mean())
+    log(f"step mean {ms_per_step * 1e3:.1f} us, median {np.median(step_ms) * 1e3:.1f} us "
+        f"({'flushed' if args.flush else 'not flushed'}; wall {wall_s / K * 1e6:.1f} us per step with the flush); "
+        f"decode median {dec_med * 1e3:.1f} us, min {dec_min * 1e3:.1f} us, mean {dec_avg * 1e3:.1f} us")
 
     graph_us = None
     if args.graph:
@@ -551,9 +667,7 @@ def main() -> int:
         # launch work between the kernels
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step.copy()
-            step.write()
-            step.plan()
+            one_step()
             step.run()
         for _ in range(args.warmup):
             graph.replay()
@@ -570,7 +684,7 @@ def main() -> int:
     seg_tokens = pkv.partition_tokens_for(wl.num_seqs, wl.num_heads, step.max_blocks, step.desc,
                                           step.partition_tokens)
     step_gbs = nb["step"] / (ms_per_step * 1e-3) / 1e9
-    dec_gbs = nb["decode"] / (dec_avg * 1e-3) / 1e9
+    dec_gbs = nb["decode"] / (dec_med * 1e-3) / 1e9
     S = wl.num_seqs
     result = {
         "metric": "paged decode-attention KV GB/s (% of MI355X HBM peak) and tokens/s at 1 GPU",
@@ -607,7 +721,17 @@ def main() -> int:
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "context_tokens_per_s": round(wl.total_context / (ms_per_step * 1e-3), 1),
         "bytes": nb,
-        "decode_call_us": round(dec_avg * 1e3, 2),
+        "decode_call_us": round(dec_med * 1e3, 2),
+        "timing": {"flushed": bool(args.flush),
+                   "flush": ("1 GiB scratch written then read between timed steps, outside the events"
+                             if args.flush else None),
+                   "step_us": {"mean": round(ms_per_step * 1e3, 2), "median": round(float(np.median(step_ms)) * 1e3, 2),
+                               "min": round(float(step_ms.min()) * 1e3, 2)},
+                   "decode_call_us": {"median": round(dec_med * 1e3, 2), "min": round(dec_min * 1e3, 2),
+                                      "mean": round(dec_avg * 1e3, 2)},
+                   "decode_gbs_at_min": round(nb["decode"] / (dec_min * 1e-3) / 1e9, 2),
+                   "events": "HIP events on the stream the kernels run on, around each step and each "
+                             "paged_attn_decode_run call"},
         "graph_step_us": None if graph_us is None else round(graph_us, 2),
         "roofline": {
             "bound": "hbm",
@@ -625,7 +749,17 @@ def main() -> int:
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        bits = harness.to_host_bits(step.out)  # the output of the last timed step, widened exactly
+        if wl.dtype == "fp16":
+            got = bits.view(np.float16).astype(np.float64)
+        else:
+            got = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+        cb = cpu_baseline(wl, args.cpu_seconds, nb, gpu_out=got)
+        tol = 2e-3 if wl.dtype == "fp16" else 1e-2
+        cb["tolerance"] = tol
+        cb["within_tolerance"] = bool(cb["max_abs_err"] <= tol)
+        result["cpu_baseline"] = cb
+        result["max_abs_err"] = cb["max_abs_err"]
     print(json.dumps(result), flush=True)
     return 0
 
