@@ -3,9 +3,10 @@
 
 One step = the GPU calls of a decode step over one synthetic batch with every
 input already resident in HBM: copy_blocks (copy-on-write pairs),
-reshape_and_cache (the new tokens), paged_attn_decode_plan (the batch's work
-list) and paged_attn_decode_run (the attention; segments of long rows merged
-by the log-sum-exp reduce).  The roofline figure is for the attention run
+reshape_and_cache (the new tokens) and paged_attn_decode_plan (the batch's work
+list), issued as one decode_step_prologue launch over a 16-bit cache, then
+paged_attn_decode_run (the attention; segments of long rows merged by the
+log-sum-exp reduce).  The roofline figure is for the attention run
 alone, timed with HIP events on the stream it runs on.
 Default workload: the LLaMA-13B-shaped batch (128 sequences, 40 MHA heads,
 head 128, block 16, fp16, lognormal contexts with median 600 capped at 2048,
@@ -629,9 +630,12 @@ def main() -> int:
             torch.sum(scratch.view(torch.int64), dim=0, keepdim=True, out=sink)
 
     def one_step():
-        step.copy()
-        step.write()
-        step.plan()
+        if step.fp8:
+            step.copy()
+            step.write()
+            step.plan()
+        else:  # the same three operations in one launch
+            step.prologue()
 
     for i in range(args.warmup):
         flush(i)
@@ -712,7 +716,8 @@ def main() -> int:
                                                          step.partition_tokens),
             "copy_pairs": int(step.block_pairs_host.shape[0]),
             "kv_cache_dtype": wl.kv_dtype,
-            "step": ("copy_blocks + reshape_and_cache + paged_attn_decode_plan + paged_attn_decode_run"
+            "step": ("decode_step_prologue (copy_blocks + reshape_and_cache + paged_attn_decode_plan in one "
+                     "launch) + paged_attn_decode_run"
                      if wl.kv_dtype == wl.dtype else
                      "copy_blocks + reshape_and_cache_fp8 + paged_attn_decode_plan + paged_attn_decode_run_fp8"),
             "parallelism": "single GPU",

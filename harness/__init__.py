@@ -99,6 +99,13 @@ class GpuStep:
         pkv.paged_attn_decode_plan(self.context_lens, self.wl.num_heads, self.max_blocks, self.k_cache,
                                    self.workspace, partition_tokens=self.partition_tokens, stream=stream)
 
+    def prologue(self, stream=None):
+        """The copy, the write and the plan in one launch (decode_step_prologue;
+        16-bit caches)."""
+        pkv.decode_step_prologue(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slot_mapping,
+                                 self.block_pairs, self.context_lens, self.wl.num_heads, self.max_blocks,
+                                 self.workspace, partition_tokens=self.partition_tokens, stream=stream)
+
     def run(self, out=None, stream=None):
         """Attention from the planned work list (paged_attn_decode_run[_fp8])."""
         out = self.out if out is None else out

@@ -305,6 +305,29 @@ pkv_status paged_attn_decode_run_fp8(void* out, const void* q, const void* k_cac
                                      int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/* decode_step_prologue — what a decode step runs before its attention, in one
+ * launch: copy_blocks(block_pairs), then reshape_and_cache(k, v,
+ * slot_mapping), then paged_attn_decode_plan(context_lens, ...) into the
+ * workspace ([blog] item 2: a block shared by parallel samples is copied
+ * before a sample writes into it).  Arguments, contracts and results are
+ * those of the three calls in that order (then call paged_attn_decode_run
+ * with the same workspace), with one more condition: a token written into the
+ * SOURCE block of a pair lies at an offset that is also written in that
+ * pair's destination.  A decode step satisfies it: the samples that share a
+ * partial block append at the same position, the copies into their fresh
+ * blocks and the last sample in place.  16-bit caches only
+ * (PKV_ERR_UNSUPPORTED for an fp8 cache).  With more than 65,536 tokens the
+ * three kernels are launched separately (the fused copy reads the whole slot
+ * mapping per copied page).  num_pairs == 0, num_tokens == 0 and num_seqs == 0
+ * are allowed. */
+pkv_status decode_step_prologue(const void* k, const void* v, void* k_cache, void* v_cache,
+                                const int32_t* slot_mapping, int32_t num_tokens,
+                                const int32_t* block_pairs, int32_t num_pairs,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* ---------------------------------------------------------------------------
  * paged_attn_prefill — multi-token-query attention over the paged cache, for
  * chunked prefill ([repo] §2.2: the prefill of a long prompt is cut into

@@ -90,6 +90,8 @@ SIGNATURES = {
     "paged_attn_decode_run_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _SP,
                                          _i32, _vp, _sz, _vp]),
     "copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _DP, _vp]),
+    "decode_step_prologue": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _DP, _i32, _vp,
+                                    _sz, _vp]),
     "swap_blocks": (_i32, [_vp, _vp, _DP, _vp, _vp, _DP, _vp, _i32, _vp]),
     "gather_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _DP, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -350,10 +352,12 @@ def paged_attn_decode_plan(context_lens, num_heads: int, max_blocks_per_seq: int
     n = int(context_lens.shape[0])
     if _validate.enabled():
         _validate.check_lengths(context_lens, max_blocks_per_seq)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:  # None: the call needs no workspace (a batch run without a plan)
+        ws_ptr, ws_bytes = _gpu(workspace, "workspace"), workspace.numel() * workspace.element_size()
     st = lib().paged_attn_decode_plan(_gpu(context_lens, "context_lens", torch.int32, 1), n, int(num_heads),
                                       int(max_blocks_per_seq), ctypes.byref(desc), int(partition_tokens),
-                                      _gpu(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                                      _stream_handle(stream))
+                                      ws_ptr, ws_bytes, _stream_handle(stream))
     _check(st, "paged_attn_decode_plan")
 
 
@@ -502,6 +506,42 @@ def copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
                            _gpu(block_pairs, "block_pairs", torch.int32, 2), n, ctypes.byref(desc),
                            _stream_handle(stream))
     _check(st, "copy_blocks")
+
+
+def decode_step_prologue(k, v, k_cache, v_cache, slot_mapping, block_pairs, context_lens, num_heads: int,
+                         max_blocks_per_seq: int, workspace, *, partition_tokens: int = 0, stream=None):
+    """copy_blocks(block_pairs), reshape_and_cache(k, v, slot_mapping) and
+    paged_attn_decode_plan(context_lens, ...) into `workspace`, in one launch
+    (16-bit caches; see pagedkv.h for the one extra condition)."""
+    torch = _torch()
+    desc = _desc_of(k_cache)
+    n = int(slot_mapping.shape[0])
+    if tuple(k.shape) != (n, desc.num_kv_heads, HEAD_SIZE) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k, v must be [num_tokens, num_kv_heads, 128]")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [num_pairs, 2]")
+    npairs = int(block_pairs.shape[0])
+    S = int(context_lens.shape[0])
+    if _validate.enabled():
+        _validate.check_slots(slot_mapping, desc.num_blocks)
+        if npairs:
+            _validate.check_copy_pairs(block_pairs, desc.num_blocks)
+            _validate.check_prologue_sources(block_pairs, slot_mapping)
+        if S:
+            _validate.check_lengths(context_lens, max_blocks_per_seq)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _gpu(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    row_dtype = None if desc.dtype == PKV_FP8_E4M3 else k_cache.dtype  # fp8: the library refuses the cache
+    st = lib().decode_step_prologue(_gpu(k, "k", row_dtype), _gpu(v, "v", row_dtype),
+                                    _gpu(k_cache, "k_cache"), _gpu(v_cache, "v_cache", k_cache.dtype),
+                                    _gpu(slot_mapping, "slot_mapping", torch.int32, 1), n,
+                                    _gpu(block_pairs, "block_pairs", torch.int32, 2) if npairs else None, npairs,
+                                    _gpu(context_lens, "context_lens", torch.int32, 1), S, int(num_heads),
+                                    int(max_blocks_per_seq), ctypes.byref(desc), int(partition_tokens), ws_ptr,
+                                    ws_bytes, _stream_handle(stream))
+    _check(st, "decode_step_prologue")
 
 
 def swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, *, stream=None):

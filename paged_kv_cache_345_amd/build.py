@@ -23,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "decode.hip", "prefill.hip", "plan.hip", "cache_ops.hip", "block_manager.cpp"]
+SOURCES = ["api.hip", "decode.hip", "prefill.hip", "plan.hip", "cache_ops.hip", "step.hip", "block_manager.cpp"]
 
 COMMON = ["-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -179,6 +179,9 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int
 
 namespace {
 
+// The plan's wave-per-chunk path applies (plan_body.h): one sequence per thread.
+bool plan_scan_fits(int32_t num_seqs, const DecodeLayout&, int threads) { return num_seqs <= threads; }
+
 // Checks shared by the plan and the run entry points.
 pkv_status check_workspace(const DecodeLayout& L, const void* workspace, size_t workspace_bytes) {
   if (L.total > 0 && (!workspace || workspace_bytes < L.total || !aligned16(workspace))) return PKV_ERR_INVALID;
@@ -197,6 +200,7 @@ pkv_status launch_plan(const DecodeLayout& L, const int32_t* context_lens, int32
   pa.max_blocks_per_seq = max_blocks_per_seq;
   pa.blocks_per_part = L.bpp;
   pa.parts_max = L.parts;
+  pa.scan = plan_scan_fits(num_seqs, L, pkv::kPlanThreads) ? 1 : 0;
   return from_hip(pkv::launch_decode_plan(pa, stream));
 }
 
@@ -454,6 +458,81 @@ pkv_status gather_cache(void* k_out, void* v_out, const void* k_cache, const voi
   return from_hip(pkv::launch_gather_cache(k_out, v_out, k_cache, v_cache, block_tables, context_lens, num_seqs,
                                            max_blocks_per_seq, out_offsets, cache->num_kv_heads, cache->num_blocks,
                                            is_fp8(cache), static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The plan of a call fits the fused prologue's plan work-group (its LDS tables).
+bool step_plan_fits(const DecodeLayout& L, int32_t num_seqs) {
+  const int64_t chunks = (static_cast<int64_t>(num_seqs) + 63) / 64;
+  return num_seqs <= pkv::kStepPlanMaxSeqs && L.parts <= pkv::kStepPlanMaxParts &&
+         (static_cast<int64_t>(L.parts) + L.bpp) * chunks <= pkv::kStepPlanMaxTasks;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status decode_step_prologue(const void* k, const void* v, void* k_cache, void* v_cache,
+                                const int32_t* slot_mapping, int32_t num_tokens, const int32_t* block_pairs,
+                                int32_t num_pairs, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                int32_t max_blocks_per_seq, const pkv_cache_desc* cache, int32_t partition_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status st = check_desc(cache);
+  if (st != PKV_OK) return st;
+  if (is_fp8(cache)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_pairs < 0) return PKV_ERR_INVALID;
+  DecodeLayout L;
+  st = decode_layout(num_seqs, num_heads, max_blocks_per_seq, partition_tokens, cache, &L);
+  if (st != PKV_OK) return st;
+  if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID;
+  if (num_tokens > 0 && (!k || !v || !slot_mapping || !aligned16(k) || !aligned16(v))) return PKV_ERR_INVALID;
+  if (num_pairs > 0 && !block_pairs) return PKV_ERR_INVALID;
+  if (static_cast<int64_t>(num_pairs) * 2 * cache->num_kv_heads > INT32_MAX / 4) return PKV_ERR_INVALID;
+  const bool plan = num_seqs > 0 && L.planned;
+  if (plan) {
+    if (!context_lens) return PKV_ERR_INVALID;
+    st = check_workspace(L, workspace, workspace_bytes);
+    if (st != PKV_OK) return st;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // a bulk write keeps the separate kernels: the merge scans every token per copied page
+  if (num_tokens > 65536) {
+    st = copy_blocks(k_cache, v_cache, block_pairs, num_pairs, cache, stream);
+    if (st == PKV_OK) st = reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens, cache, stream);
+    if (st == PKV_OK && plan) st = launch_plan(L, context_lens, num_seqs, num_heads, max_blocks_per_seq, workspace, hs);
+    return st;
+  }
+  const bool fused_plan = plan && step_plan_fits(L, num_seqs);
+  pkv::StepArgs a{};
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.slot_mapping = slot_mapping;
+  a.block_pairs = block_pairs;
+  a.num_tokens = num_tokens;
+  a.num_pairs = num_pairs;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_blocks = cache->num_blocks;
+  a.planned = fused_plan ? 1 : 0;
+  if (fused_plan) {
+    a.plan.context_lens = context_lens;
+    a.plan.plan = reinterpret_cast<int*>(static_cast<char*>(workspace) + L.plan);
+    a.plan.num_seqs = num_seqs;
+    a.plan.num_heads = num_heads;
+    a.plan.units = L.units;
+    a.plan.max_blocks_per_seq = max_blocks_per_seq;
+    a.plan.blocks_per_part = L.bpp;
+    a.plan.parts_max = L.parts;
+    a.plan.scan = plan_scan_fits(num_seqs, L, pkv::kStepThreads) ? 1 : 0;
+  }
+  st = from_hip(pkv::launch_decode_step_prologue(a, hs));
+  if (st == PKV_OK && plan && !fused_plan)
+    st = launch_plan(L, context_lens, num_seqs, num_heads, max_blocks_per_seq, workspace, hs);
+  return st;
 }
 
 }  // extern "C"

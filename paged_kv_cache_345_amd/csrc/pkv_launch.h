@@ -75,11 +75,38 @@ struct PlanArgs {
   int max_blocks_per_seq;
   int blocks_per_part;
   int parts_max;
+  int scan;  // 1: at most one sequence per thread of the plan work-group (plan_body.h's wave-per-chunk path)
+};
+
+// The fused decode-step prologue (step.hip): copy_blocks, reshape_and_cache
+// and the plan in one launch over a 16-bit cache.  Its plan work-group has 256
+// threads and smaller LDS tables than decode_plan_kernel, so the launch keeps
+// 7 work-groups per compute unit for the copy and write roles.
+constexpr int kPlanThreads = 1024;  // decode_plan_kernel
+constexpr int kStepThreads = 256;   // decode_step_prologue_kernel
+constexpr int kStepPlanMaxSeqs = 1024;
+constexpr int kStepPlanMaxTasks = 2048;
+constexpr int kStepPlanMaxParts = 1024;
+struct StepArgs {
+  const uint16_t* k;  // [num_tokens, num_kv_heads, 128] new rows
+  const uint16_t* v;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const int32_t* slot_mapping;
+  const int32_t* block_pairs;  // [num_pairs][2] (src, dst)
+  int64_t num_tokens;
+  int num_pairs;
+  int num_kv_heads;
+  int32_t num_blocks;
+  int planned;      // 1: the plan work-group writes the plan
+  PlanArgs plan;
+  int64_t plan_wg;  // the plan work-group: after the write work-groups, before the copies (set by the launcher)
 };
 
 // act_dtype: 0 fp16, 1 bf16 (q, out); fp8_cache: the pages hold E4M3 codes
 hipError_t launch_decode(const DecodeArgs& a, int act_dtype, bool fp8_cache, hipStream_t stream);
 hipError_t launch_decode_plan(const PlanArgs& a, hipStream_t stream);
+hipError_t launch_decode_step_prologue(const StepArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int act_dtype, bool fp8_cache, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,

@@ -110,3 +110,20 @@ def _distinct_dsts(bp: np.ndarray) -> None:
     u, counts = np.unique(bp[:, 1], return_counts=True)
     if (counts > 1).any():
         raise ValueError(f"destination block {int(u[np.argmax(counts > 1)])} appears twice")
+
+
+def check_prologue_sources(block_pairs, slot_mapping) -> None:
+    """decode_step_prologue's extra condition: a token written into the source
+    block of a pair lies at an offset that is also written in the pair's
+    destination."""
+    bp = _host(block_pairs).astype(np.int64).reshape(-1, 2)
+    slots = _host(slot_mapping).astype(np.int64)
+    slots = slots[slots >= 0]
+    by_block = {}
+    for sl in slots.tolist():
+        by_block.setdefault(sl // BLOCK_SIZE, set()).add(sl % BLOCK_SIZE)
+    for src, dst in bp.tolist():
+        extra = by_block.get(src, set()) - by_block.get(dst, set())
+        if extra:
+            raise ValueError(f"block_pairs ({src}, {dst}): tokens are written into the source block at offsets "
+                             f"{sorted(extra)} that the destination does not receive")

@@ -215,16 +215,19 @@ def _plan_ref(lens, bpp, max_blocks):
     return list_a, list_b
 
 
-@pytest.mark.parametrize("name,pt,g", [("llama13b", 0, 1), ("random", 48, 1), ("random", 16, 1), ("random", 0, 1),
-                                       ("random", 1024, 1), ("random", 0, 4)])
-def test_plan_lists_are_exact(name, pt, g):
+@pytest.mark.parametrize("name,pt,g,S", [("llama13b", 0, 1, 128), ("random", 48, 1, 70), ("random", 16, 1, 70),
+                                         ("random", 0, 1, 70), ("random", 1024, 1, 70), ("random", 0, 4, 70),
+                                         ("random", 0, 1, 1100), ("random", 64, 2, 700)])
+def test_plan_lists_are_exact(name, pt, g, S):
     """White-box check of the work-list pre-pass (integer work, bit-exact): the
     plan at the start of the workspace lists every non-empty segment once, in
-    the documented order."""
+    the documented order.  Small batches take the plan's one-sequence-per-
+    thread path; 1,100 sequences, and 700 with 64-token segments, the general
+    one."""
     if name == "llama13b":
         wl = synth.make_workload("llama13b")
     else:
-        wl = synth.make_random_workload(4242 + pt + g, num_seqs=70, num_heads=2 * g, num_kv_heads=2,
+        wl = synth.make_random_workload(4242 + pt + g + S, num_seqs=S, num_heads=2 * g, num_kv_heads=2,
                                         dtype="fp16", max_len=900, min_len=1, groups=3)
     step = harness.build_step(wl, partition_tokens=pt)
     desc = step.desc

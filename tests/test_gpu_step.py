@@ -1,0 +1,134 @@
+"""The fused decode-step prologue (decode_step_prologue: the copy-on-write
+block copy, the slot-mapped write and the work-list plan in one launch)
+against the three separate calls.  Marked gpu.
+
+Both start from the same caches (every prior token written, garbage in every
+other slot) and the same workspace contents; afterwards both whole caches,
+the plan section of the workspace and the attention outputs must be
+bit-identical.  Batches: random shapes with parallel-sample groups of 2 to 9
+members (several copies of one source block, the last sample writing in
+place, prompts ending on a block boundary), padding slots, the LLaMA-13B-shaped
+batch at full size, and batch sizes on both sides of the fused plan's
+capacity and of the plan's own.  The cache contents after the step are the
+oracle's as well (tests/test_gpu_cache_ops.py checks the separate calls
+against the oracle bit for bit).
+"""
+
+import numpy as np
+import pytest
+
+import harness
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import paged_kv_cache_345_amd as pkv  # noqa: E402
+
+
+def _pair(wl, pt=None):
+    """Two copies of the same state before the step, with the same garbage."""
+    a = harness.build_step(wl, garbage="random", garbage_seed=5, partition_tokens=pt, run=False)
+    b = harness.build_step(wl, garbage="random", garbage_seed=5, partition_tokens=pt, run=False)
+    for st in (a, b):
+        if st.workspace is not None:
+            st.workspace.fill_(0x5A)
+    torch.cuda.synchronize()
+    assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
+    return a, b
+
+
+def _compare(a, b):
+    # a: separate calls; b: one prologue launch
+    a.copy()
+    a.write()
+    a.plan()
+    b.prologue()
+    oa, ob = a.run(out=torch.full_like(a.out, 7.0)), b.run(out=torch.full_like(b.out, 9.0))
+    torch.cuda.synchronize()
+    assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
+    assert torch.equal(a.v_cache.view(torch.int16), b.v_cache.view(torch.int16))
+    if a.workspace is not None:
+        assert torch.equal(a.workspace, b.workspace)
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+@pytest.mark.parametrize("gs,g,dtype", [(2, 1, "fp16"), (3, 1, "fp16"), (4, 4, "bf16"), (5, 1, "bf16"),
+                                        (9, 2, "fp16"), (3, 8, "bf16")])
+def test_sample_groups(gs, g, dtype):
+    wl = synth.make_random_workload(9400 + 10 * gs + g, num_seqs=3 * gs + 7, num_heads=3 * g, num_kv_heads=3,
+                                    dtype=dtype, max_len=700, min_len=1, groups=3, group_size=gs)
+    a, b = _pair(wl)
+    assert a.block_pairs_host.shape[0] > 0
+    _compare(a, b)
+
+
+@pytest.mark.parametrize("pt", [0, 16, 64])
+def test_forced_segments(pt):
+    wl = synth.make_random_workload(9500 + pt, num_seqs=12, num_heads=4, num_kv_heads=2, dtype="fp16",
+                                    max_len=1500, min_len=1, groups=2)
+    a, b = _pair(wl, pt)
+    _compare(a, b)
+
+
+def test_llama13b_full_size():
+    wl = synth.make_workload("llama13b")
+    a, b = _pair(wl)
+    assert a.block_pairs_host.shape == (22, 2)
+    _compare(a, b)
+
+
+@pytest.mark.parametrize("num_seqs", [200, 300, 1024, 1025, 4097])
+def test_plan_capacity_edges(num_seqs):
+    """200 sequences: the plan's one-sequence-per-thread path in both; 300:
+    the general path inside the launch against that path in the plan kernel;
+    1024: the general path in both; 1025: the plan kernel is launched after
+    the fused one; 4097: no plan (direct mode)."""
+    wl = synth.make_random_workload(9600 + num_seqs, num_seqs=num_seqs, num_heads=2, num_kv_heads=2,
+                                    dtype="bf16", max_len=60, min_len=1, groups=5, group_size=3)
+    a, b = _pair(wl)
+    _compare(a, b)
+
+
+def test_padding_slots_and_empty_parts():
+    """Padding entries (-1) in the slot mapping, no copy pairs, then no tokens."""
+    wl = synth.make_random_workload(9700, num_seqs=9, num_heads=8, num_kv_heads=2, dtype="fp16", max_len=300,
+                                    min_len=1, groups=0)
+    a, b = _pair(wl)
+    assert a.block_pairs_host.shape[0] == 0
+    sm = a.slot_mapping.clone()
+    sm[[1, 4]] = -1
+    for st in (a, b):
+        st.slot_mapping = sm
+    _compare(a, b)
+    for st in (a, b):
+        st.slot_mapping = sm[:0]
+        st.k_new, st.v_new = st.k_new[:0], st.v_new[:0]
+    _compare(a, b)
+
+
+def test_fp8_cache_is_refused():
+    wl = synth.make_random_workload(9800, num_seqs=3, num_heads=2, num_kv_heads=2, dtype="fp16", max_len=40,
+                                    kv_dtype="fp8e4m3", k_scale=0.0125, v_scale=0.02)
+    st = harness.build_step(wl, run=False)
+    with pytest.raises(pkv.PagedKVError):
+        st.prologue()
+
+
+def test_validate_mode_checks_the_extra_condition(monkeypatch):
+    """PKV_VALIDATE=1: a token written into a copy source at an offset its
+    destination does not receive is refused before the launch."""
+    monkeypatch.setenv("PKV_VALIDATE", "1")
+    wl = synth.make_random_workload(9900, num_seqs=6, num_heads=2, num_kv_heads=2, dtype="fp16", max_len=200,
+                                    min_len=20, groups=2)
+    st = harness.build_step(wl, run=False)
+    st.prologue()  # a decode step satisfies the condition
+    torch.cuda.synchronize()
+    src, dst = (int(x) for x in st.block_pairs_host[0])
+    sm = st.slot_mapping_host.copy()
+    i = int(np.nonzero(sm // 16 == dst)[0][0])
+    j = (i + 1) % len(sm)
+    sm[j] = src * 16 + ((sm[i] % 16) + 1) % 16  # another offset of the source block
+    st.slot_mapping = torch.from_numpy(sm).cuda()
+    with pytest.raises(ValueError, match="source block"):
+        st.prologue()
