@@ -9,11 +9,13 @@ plainest readings, stated here and in the tests:
   bits with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals
   (m / 8) * 2^-6; there are no infinities; S.1111.111 is NaN; the largest
   finite magnitude is 448;
-* scaling: one float32 scale per cache (``k_scale`` for K, ``v_scale`` for V);
-  the stored code of a value x is the E4M3 value nearest to the float32
-  quotient x / scale (one IEEE float32 division), ties to the even mantissa,
+* scaling: a float32 scale for K and one for V, either one per cache or one
+  per KV head (``k_scale`` / ``v_scale`` given as a float, or as a sequence of
+  ``num_kv_heads`` floats, element h applying to every row of KV head h); the
+  stored code of a value x of head h is the E4M3 value nearest to the float32
+  quotient x / scale_h (one IEEE float32 division), ties to the even mantissa,
   finite magnitudes beyond 448 saturated to 448, the sign of zero kept; the
-  value a code stands for is decode(code) * scale;
+  value a code stands for is decode(code) * scale_h;
 * attention over an fp8 cache is the same softmax attention (``attention_ref``)
   over the dequantised rows, in float64; queries and outputs stay fp16/bf16.
 
@@ -22,7 +24,9 @@ representable value by search over the sorted finite values, not by bit
 manipulation.  Pins (``tests/test_oracle_fp8.py``): the closed-form values the
 definition fixes (1, 448, 2^-6, 2^-9, -0, NaN), brute-force nearest-value
 search over all codes, and torch's own float8_e4m3fn conversion where its
-semantics coincide (every decode; encodes below the saturation bound).
+semantics coincide (every decode; encodes below the saturation bound).  Per-head
+scales reduce, head by head, to the one-scale case (pinned the same way), and
+equal per-head scales give exactly the one-scale results.
 """
 
 from __future__ import annotations
@@ -92,11 +96,28 @@ def e4m3_decode(codes) -> np.ndarray:
     return e4m3_table()[np.asarray(codes, dtype=np.uint8).astype(np.int64)]
 
 
-def quantize_ref(x: np.ndarray, act_dtype: str, scale: float) -> np.ndarray:
-    """E4M3 codes of stored fp16/bf16 values x under a float32 scale: the
-    nearest code to float32(x) / float32(scale)."""
+def head_scales(scale, rows: np.ndarray) -> np.ndarray:
+    """The float32 scale as an array that broadcasts over rows [..., Hkv, D]:
+    a 0-d array for one scale per cache, [Hkv, 1] for one scale per KV head."""
+    s = np.asarray(scale, dtype=np.float32)
+    if s.ndim == 0:
+        return s
+    if rows.ndim < 2 or s.shape != (rows.shape[-2],):
+        raise ValueError(f"per-head scales of shape {s.shape} do not match rows of shape {rows.shape}")
+    return s[:, None]
+
+
+def quantize_ref(x: np.ndarray, act_dtype: str, scale) -> np.ndarray:
+    """E4M3 codes of stored fp16/bf16 rows x [..., Hkv, D] under a float32
+    scale per cache or per KV head: the nearest code to float32(x) /
+    float32(scale of the row's head)."""
     xf = to_f64(x, act_dtype).astype(np.float32)  # exact: fp16 and bf16 fit float32
-    return e4m3_encode(xf / np.float32(scale))
+    return e4m3_encode(xf / head_scales(scale, xf))
+
+
+def dequantize_ref(codes: np.ndarray, scale) -> np.ndarray:
+    """float64 values of codes [..., Hkv, D]: decode(code) * the row head's scale."""
+    return e4m3_decode(codes) * head_scales(scale, np.asarray(codes)).astype(np.float64)
 
 
 def new_fp8_cache(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int, fill: int = 0):
@@ -104,9 +125,10 @@ def new_fp8_cache(num_blocks: int, block_size: int, num_kv_heads: int, head_size
     return np.full(shape, fill, dtype=np.uint8), np.full(shape, fill, dtype=np.uint8)
 
 
-def scatter_fp8_ref(k_cache8, v_cache8, k, v, slot_mapping, act_dtype: str, k_scale: float, v_scale: float):
+def scatter_fp8_ref(k_cache8, v_cache8, k, v, slot_mapping, act_dtype: str, k_scale, v_scale):
     """The slot-mapped write into an fp8 cache: for each token i with slot >= 0,
-    block slot // bs, offset slot % bs receives the codes of k[i], v[i]."""
+    block slot // bs, offset slot % bs receives the codes of k[i], v[i]
+    (scales per cache or per KV head)."""
     bs = k_cache8.shape[1]
     for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
         if slot < 0:
@@ -117,22 +139,19 @@ def scatter_fp8_ref(k_cache8, v_cache8, k, v, slot_mapping, act_dtype: str, k_sc
 
 def paged_decode_fp8_ref(q: np.ndarray, k_cache8: np.ndarray, v_cache8: np.ndarray, block_tables: np.ndarray,
                          context_lens: Sequence[int], scale: float, num_kv_heads: int, act_dtype: str,
-                         k_scale: float, v_scale: float, seqs: Sequence[int] = None) -> np.ndarray:
+                         k_scale, v_scale, seqs: Sequence[int] = None) -> np.ndarray:
     """Paged decode attention over an fp8 cache: the rows gathered through the
-    block table are dequantised (decode(code) * scale, float64) and attended to
-    with the plain softmax definition.  Returns float64 [len(seqs), Hq, D]."""
+    block table are dequantised (decode(code) * the scale of the row's head,
+    float64) and attended to with the plain softmax definition.  Returns
+    float64 [len(seqs), Hq, D]."""
     S, hq, d = q.shape
     assert k_cache8.dtype == np.uint8 and k_cache8.shape[2] == num_kv_heads
     if seqs is None:
         seqs = range(S)
-    table = e4m3_table()
-    ks, vs = np.float64(np.float32(k_scale)), np.float64(np.float32(v_scale))
     out = []
     for s in seqs:
         L = int(context_lens[s])
-        kc = gather_seq(k_cache8, block_tables[s], L)
-        vc = gather_seq(v_cache8, block_tables[s], L)
-        k = table[kc.astype(np.int64)] * ks
-        v = table[vc.astype(np.int64)] * vs
+        k = dequantize_ref(gather_seq(k_cache8, block_tables[s], L), k_scale)
+        v = dequantize_ref(gather_seq(v_cache8, block_tables[s], L), v_scale)
         out.append(attention_ref(to_f64(q[s], act_dtype), k, v, scale))
     return np.stack(out)

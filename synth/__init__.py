@@ -33,7 +33,7 @@ import math
 import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
-from typing import Dict, List, Optional, Sequence, Tuple
+from typing import Dict, List, Optional, Sequence, Tuple, Union
 
 import numpy as np
 
@@ -122,8 +122,13 @@ class ConfigSpec:
     partition_tokens: int = 0  # 0: library default
     description: str = ""
     kv_dtype: Optional[str] = None  # "fp8e4m3": the cache stores E4M3 codes of the rows
-    k_scale: float = 1.0  # fp8 cache: dequantised K = code value * k_scale
-    v_scale: float = 1.0
+    # fp8 cache: dequantised K = code value * k_scale, one float per cache or a
+    # tuple of one float per KV head (likewise V)
+    k_scale: Union[float, Tuple[float, ...]] = 1.0
+    v_scale: Union[float, Tuple[float, ...]] = 1.0
+    # > 0: the K scale of KV head h is this times the batch's key scale of
+    # head h (per-head scales that follow the heads' key magnitudes)
+    k_scale_per_key_scale: float = 0.0
 
     @property
     def group_size(self) -> int:
@@ -174,9 +179,10 @@ CONFIGS["llama13b_fp8"] = replace(
                 "fp16 queries, lognormal contexts (median 600, cap 2048), 13 groups of 3 parallel "
                 "samples, K/V scales 0.0125")
 CONFIGS["gqa_fp8"] = replace(
-    CONFIGS["gqa"], name="gqa_fp8", kv_dtype="fp8e4m3", k_scale=0.025, v_scale=0.0125,
+    CONFIGS["gqa"], name="gqa_fp8", kv_dtype="fp8e4m3", k_scale_per_key_scale=0.0125, v_scale=0.0125,
     description="GQA decode batch over an fp8 (E4M3) cache: 256 seqs, 64 query / 8 KV heads, bf16 "
-                "queries, contexts U[1024,8192], per-KV-head key scale U[0.5,2], K scale 0.025, V scale 0.0125")
+                "queries, contexts U[1024,8192], per-KV-head key scale U[0.5,2]; per-KV-head K scales "
+                "0.0125 x the head's key scale, one V scale 0.0125")
 
 
 # --------------------------------------------------------------------------
@@ -226,12 +232,15 @@ class Workload:
         return self.spec.kv_dtype or self.spec.dtype
 
     @property
-    def k_scale(self) -> float:
-        return self.spec.k_scale
+    def k_scale(self):
+        """fp8 cache: the K scale, a float (one per cache) or float32 [Hkv]."""
+        if self.spec.k_scale_per_key_scale > 0:
+            return (np.float32(self.spec.k_scale_per_key_scale) * self.key_scales).astype(np.float32)
+        return _scale_value(self.spec.k_scale)
 
     @property
-    def v_scale(self) -> float:
-        return self.spec.v_scale
+    def v_scale(self):
+        return _scale_value(self.spec.v_scale)
 
     @property
     def pool_blocks(self) -> int:
@@ -300,6 +309,15 @@ class Workload:
     @property
     def total_context(self) -> int:
         return int(self.context_lens.sum())
+
+
+def _scale_value(x):
+    """A float stays a float; a tuple of per-head scales becomes float32 [Hkv]."""
+    return np.asarray(x, dtype=np.float32) if isinstance(x, (tuple, list, np.ndarray)) else float(x)
+
+
+def _as_spec_scale(x):
+    return tuple(float(v) for v in x) if isinstance(x, (tuple, list, np.ndarray)) else float(x)
 
 
 def _draw_lengths(spec: ConfigSpec, rng: np.random.Generator):
@@ -372,8 +390,8 @@ def make_workload(name_or_spec, *, with_q: bool = True) -> Workload:
 def make_random_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_heads: int,
                          dtype: str, max_len: int, pool_slack: int = 4,
                          min_len: int = 1, groups: int = 0, group_size: int = 3,
-                         key_scale=None, kv_dtype: Optional[str] = None, k_scale: float = 1.0,
-                         v_scale: float = 1.0) -> Workload:
+                         key_scale=None, kv_dtype: Optional[str] = None, k_scale=1.0,
+                         v_scale=1.0) -> Workload:
     """Small random workload for property tests: lengths U[min_len, max_len],
     optionally the first group_size*groups sequences in sampling groups of
     group_size."""
@@ -390,7 +408,8 @@ def make_random_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_hea
     spec = ConfigSpec(name=f"random{seed}", seed=seed, num_seqs=num_seqs, num_heads=num_heads,
                       num_kv_heads=num_kv_heads, dtype=dtype,
                       lengths=("fixed", tuple(int(v) for v in lens)), pool_blocks=pool,
-                      key_scale=key_scale, kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
+                      key_scale=key_scale, kv_dtype=kv_dtype, k_scale=_as_spec_scale(k_scale),
+                      v_scale=_as_spec_scale(v_scale))
     free_order = rng.permutation(pool).astype(np.int32)
     key_scales = None
     if key_scale is not None:
@@ -425,8 +444,8 @@ class PrefillWorkload:
     key_scales: Optional[np.ndarray] = None
     description: str = ""
     kv_dtype: Optional[str] = None  # "fp8e4m3": the cache holds E4M3 codes of the rows
-    k_scale: float = 1.0
-    v_scale: float = 1.0
+    k_scale: Union[float, np.ndarray] = 1.0  # a float (one per cache) or float32 [Hkv]
+    v_scale: Union[float, np.ndarray] = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -462,8 +481,9 @@ class PrefillWorkload:
 def make_prefill_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_heads: int, dtype: str,
                           context: Tuple[int, int], chunk: Tuple[int, int], key_scale=None, pool_slack: int = 4,
                           name: str = "", description: str = "", kv_dtype: Optional[str] = None,
-                          k_scale: float = 1.0, v_scale: float = 1.0) -> PrefillWorkload:
-    """Contexts U[context], chunk lengths U[chunk] clipped to the context."""
+                          k_scale=1.0, v_scale=1.0) -> PrefillWorkload:
+    """Contexts U[context], chunk lengths U[chunk] clipped to the context.  fp8
+    scales: a float, or one float per KV head."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(context[0], context[1], num_seqs, endpoint=True).astype(np.int64)
     chunks = np.minimum(rng.integers(chunk[0], chunk[1], num_seqs, endpoint=True), lens).astype(np.int64)
@@ -475,8 +495,8 @@ def make_prefill_workload(seed: int, *, num_seqs: int, num_heads: int, num_kv_he
     q = _to_storage(rng.standard_normal((int(chunks.sum()), num_heads, HEAD_SIZE), dtype=np.float32), dtype)
     return PrefillWorkload(name=name or f"prefill{seed}", seed=seed, num_heads=num_heads, num_kv_heads=num_kv_heads,
                            dtype=dtype, context_lens=lens, chunk_lens=chunks, free_order=free_order, q=q,
-                           key_scales=key_scales, description=description, kv_dtype=kv_dtype, k_scale=k_scale,
-                           v_scale=v_scale)
+                           key_scales=key_scales, description=description, kv_dtype=kv_dtype,
+                           k_scale=_scale_value(k_scale), v_scale=_scale_value(v_scale))
 
 
 PREFILL_CONFIGS = {

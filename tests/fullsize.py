@@ -28,8 +28,8 @@ def seq_rows_f64(wl, s):
     fp8 cache (the oracle's encoder and decoder)."""
     k, v = wl.seq_kv(s)
     if wl.kv_dtype == "fp8e4m3":
-        kf = ofp8.e4m3_decode(ofp8.quantize_ref(k, wl.dtype, wl.k_scale)) * np.float64(np.float32(wl.k_scale))
-        vf = ofp8.e4m3_decode(ofp8.quantize_ref(v, wl.dtype, wl.v_scale)) * np.float64(np.float32(wl.v_scale))
+        kf = ofp8.dequantize_ref(ofp8.quantize_ref(k, wl.dtype, wl.k_scale), wl.k_scale)
+        vf = ofp8.dequantize_ref(ofp8.quantize_ref(v, wl.dtype, wl.v_scale), wl.v_scale)
         return kf, vf
     return oracle.to_f64(k, wl.dtype), oracle.to_f64(v, wl.dtype)
 

@@ -40,8 +40,8 @@ def _ref_rows(wl, seqs=None, heads=None):
     for s in (range(wl.num_seqs) if seqs is None else seqs):
         k, v = wl.seq_kv(s)
         if wl.kv_dtype == "fp8e4m3":
-            kf = ofp8.e4m3_decode(ofp8.quantize_ref(k, wl.dtype, wl.k_scale)) * np.float64(np.float32(wl.k_scale))
-            vf = ofp8.e4m3_decode(ofp8.quantize_ref(v, wl.dtype, wl.v_scale)) * np.float64(np.float32(wl.v_scale))
+            kf = ofp8.dequantize_ref(ofp8.quantize_ref(k, wl.dtype, wl.k_scale), wl.k_scale)
+            vf = ofp8.dequantize_ref(ofp8.quantize_ref(v, wl.dtype, wl.v_scale), wl.v_scale)
         else:
             kf, vf = oracle.to_f64(k, wl.dtype), oracle.to_f64(v, wl.dtype)
         L, C = int(wl.context_lens[s]), int(wl.chunk_lens[s])
@@ -181,8 +181,8 @@ def _ref_rows_at(wl, s, rows, heads):
     g = wl.num_heads // wl.num_kv_heads
     k, v = wl.seq_kv(s)
     if wl.kv_dtype == "fp8e4m3":
-        kf = ofp8.e4m3_decode(ofp8.quantize_ref(k, wl.dtype, wl.k_scale)) * np.float64(np.float32(wl.k_scale))
-        vf = ofp8.e4m3_decode(ofp8.quantize_ref(v, wl.dtype, wl.v_scale)) * np.float64(np.float32(wl.v_scale))
+        kf = ofp8.dequantize_ref(ofp8.quantize_ref(k, wl.dtype, wl.k_scale), wl.k_scale)
+        vf = ofp8.dequantize_ref(ofp8.quantize_ref(v, wl.dtype, wl.v_scale), wl.v_scale)
     else:
         kf, vf = oracle.to_f64(k, wl.dtype), oracle.to_f64(v, wl.dtype)
     L, C = int(wl.context_lens[s]), int(wl.chunk_lens[s])

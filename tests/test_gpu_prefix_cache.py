@@ -27,8 +27,8 @@ TOL = {"fp16": 2e-3, "bf16": 1e-2}
 
 def _rows_f64(wl, k, v):
     if wl.kv_dtype == "fp8e4m3":
-        return (ofp8.e4m3_decode(ofp8.quantize_ref(k, wl.dtype, wl.k_scale)) * np.float64(np.float32(wl.k_scale)),
-                ofp8.e4m3_decode(ofp8.quantize_ref(v, wl.dtype, wl.v_scale)) * np.float64(np.float32(wl.v_scale)))
+        return (ofp8.dequantize_ref(ofp8.quantize_ref(k, wl.dtype, wl.k_scale), wl.k_scale),
+                ofp8.dequantize_ref(ofp8.quantize_ref(v, wl.dtype, wl.v_scale), wl.v_scale))
     return oracle.to_f64(k, wl.dtype), oracle.to_f64(v, wl.dtype)
 
 

@@ -186,3 +186,91 @@ def test_fp8_step_equals_brute_force_on_dequantised_rows(dtype, groups):
         vd = fp8.e4m3_decode(fp8.quantize_ref(v, dtype, wl.v_scale)) * np.float64(np.float32(wl.v_scale))
         ref = oracle.brute_force_ref(oracle.to_f64(wl.q[s], dtype), kd, vd, wl.scale)
         np.testing.assert_allclose(st.out[s], ref, rtol=0, atol=1e-12)
+
+
+# --- per-KV-head scales --------------------------------------------------
+
+
+def _rows(seed, n=40, hkv=3, dtype="fp16", spread=(0.25, 4.0)):
+    rng = np.random.default_rng(seed)
+    s = rng.uniform(*spread, hkv).astype(np.float32)
+    x = (rng.standard_normal((n, hkv, 128)) * s[None, :, None]).astype(np.float32)
+    return (x.astype(np.float16) if dtype == "fp16" else synth_bf16(x)), s
+
+
+def synth_bf16(x):
+    import synth
+    return synth.round_bf16_bits(x)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_per_head_codes_are_the_one_scale_codes_head_by_head(dtype):
+    """Each head's codes under its own scale are exactly the codes of that
+    head's rows quantised alone with that one scale (the pinned case)."""
+    x, s = _rows(21, dtype=dtype)
+    scales = (0.01 * s).astype(np.float32)
+    codes = fp8.quantize_ref(x, dtype, scales)
+    for h in range(x.shape[1]):
+        assert np.array_equal(codes[:, h], fp8.quantize_ref(x[:, h], dtype, float(scales[h])))
+    # and against torch's encoder on the float32 quotient of each head
+    xf = oracle.to_f64(x, dtype).astype(np.float32) / scales[None, :, None]
+    below = np.abs(xf) < fp8.E4M3_MAX
+    ref = torch.from_numpy(xf).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes[below], ref[below])
+
+
+def test_equal_per_head_scales_equal_one_scale():
+    x, _ = _rows(22)
+    a = fp8.quantize_ref(x, "fp16", 0.03)
+    b = fp8.quantize_ref(x, "fp16", np.full(3, 0.03, np.float32))
+    assert np.array_equal(a, b)
+    codes = a[:, None]  # [L, 1 token slot, ...] -> decode through the per-head path
+    assert np.array_equal(fp8.dequantize_ref(a, 0.03), fp8.dequantize_ref(a, [0.03, 0.03, 0.03]))
+    del codes
+
+
+def test_per_head_scales_planted_mistakes():
+    """Scales applied to the wrong heads, or one scale for all, change codes."""
+    x, s = _rows(23)
+    scales = (0.01 * s).astype(np.float32)
+    good = fp8.quantize_ref(x, "fp16", scales)
+    assert not np.array_equal(good, fp8.quantize_ref(x, "fp16", scales[::-1].copy()))
+    assert not np.array_equal(good, fp8.quantize_ref(x, "fp16", float(scales.mean())))
+    with pytest.raises(ValueError):
+        fp8.quantize_ref(x, "fp16", scales[:2])
+
+
+def test_per_head_dequantised_values():
+    """decode(code) * the scale of the row's head, by explicit loops."""
+    rng = np.random.default_rng(24)
+    codes = rng.integers(0, 0x7F, (5, 4, 128)).astype(np.uint8)
+    sc = np.float32([0.5, 0.125, 0.03, 2.0])
+    got = fp8.dequantize_ref(codes, sc)
+    for t in range(5):
+        for h in range(4):
+            for d in (0, 17, 127):
+                assert got[t, h, d] == fp8.e4m3_value(codes[t, h, d]) * float(sc[h])
+
+
+@pytest.mark.parametrize("dtype,groups", [("fp16", 1), ("bf16", 0)])
+def test_fp8_step_with_per_head_scales_equals_brute_force(dtype, groups):
+    """A whole oracle decode step over an fp8 cache with per-KV-head K and V
+    scales equals the explicit-loop formula on each sequence's contiguous
+    rows, quantised and dequantised head by head."""
+    import synth
+    ks = (0.012, 0.05, 0.02)
+    vs = (0.03, 0.01, 0.02)
+    wl = synth.make_random_workload(60 + groups, num_seqs=5, num_heads=6, num_kv_heads=3, dtype=dtype,
+                                    max_len=60, groups=groups, key_scale=(0.5, 2.0), kv_dtype="fp8e4m3",
+                                    k_scale=ks, v_scale=vs)
+    assert wl.k_scale.shape == (3,)
+    st = oracle.run_decode_step(wl)
+    for s in range(wl.num_seqs):
+        k, v = wl.seq_kv(s)
+        kc, vc = fp8.quantize_ref(k, dtype, ks), fp8.quantize_ref(v, dtype, vs)
+        kd = np.stack([[fp8.e4m3_decode(kc[t, h]) * float(np.float32(ks[h])) for h in range(3)]
+                       for t in range(k.shape[0])])
+        vd = np.stack([[fp8.e4m3_decode(vc[t, h]) * float(np.float32(vs[h])) for h in range(3)]
+                       for t in range(v.shape[0])])
+        ref = oracle.brute_force_ref(oracle.to_f64(wl.q[s], dtype), kd, vd, wl.scale)
+        np.testing.assert_allclose(st.out[s], ref, rtol=0, atol=1e-12)
