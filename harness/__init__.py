@@ -35,6 +35,15 @@ def to_device(a: np.ndarray, dtype: str, device):
     return t.to(device)
 
 
+def scale_arg(x, device="cuda"):
+    """An fp8 scale as the binding takes it: a float stays a float; per-head
+    scales (a float32 array [Hkv]) become a GPU float32 tensor."""
+    import torch
+    if isinstance(x, np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+    return float(x)
+
+
 def to_host_bits(t) -> np.ndarray:
     """GPU fp16/bf16 tensor -> numpy uint16 bit patterns."""
     import torch
@@ -61,6 +70,8 @@ class GpuStep:
     block_tables_host: np.ndarray
     slot_mapping_host: np.ndarray
     block_pairs_host: np.ndarray
+    k_scale: object = 1.0  # fp8 cache: the scales as the binding takes them (float or GPU tensor)
+    v_scale: object = 1.0
 
     @property
     def desc(self):
@@ -76,7 +87,8 @@ class GpuStep:
             pkv.copy_blocks(self.k_cache, self.v_cache, self.block_pairs, stream=stream)
 
     def write(self, stream=None):
-        write_rows(self.wl, self.k_new, self.v_new, self.k_cache, self.v_cache, self.slot_mapping, stream=stream)
+        write_rows(self.wl, self.k_new, self.v_new, self.k_cache, self.v_cache, self.slot_mapping, stream=stream,
+                   scales=(self.k_scale, self.v_scale))
 
     def decode(self, out=None, stream=None, partition_tokens=None, block_tables=None, k_cache=None,
                v_cache=None, q=None):
@@ -88,7 +100,7 @@ class GpuStep:
                 self.block_tables if block_tables is None else block_tables,
                 self.context_lens, self.wl.scale, self.wl.num_kv_heads)
         if self.fp8:
-            pkv.paged_attn_decode_fp8(*args, self.wl.k_scale, self.wl.v_scale, partition_tokens=pt, workspace=ws,
+            pkv.paged_attn_decode_fp8(*args, self.k_scale, self.v_scale, partition_tokens=pt, workspace=ws,
                                       stream=stream)
         else:
             pkv.paged_attn_decode(*args, partition_tokens=pt, workspace=ws, stream=stream)
@@ -112,7 +124,7 @@ class GpuStep:
         args = (out, self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens, self.wl.scale,
                 self.wl.num_kv_heads)
         if self.fp8:
-            pkv.paged_attn_decode_run_fp8(*args, self.wl.k_scale, self.wl.v_scale, workspace=self.workspace,
+            pkv.paged_attn_decode_run_fp8(*args, self.k_scale, self.v_scale, workspace=self.workspace,
                                           partition_tokens=self.partition_tokens, stream=stream)
         else:
             pkv.paged_attn_decode_run(*args, workspace=self.workspace, partition_tokens=self.partition_tokens,
@@ -125,15 +137,17 @@ class GpuStep:
         return self.decode(stream=stream)
 
 
-def write_rows(wl, k, v, k_cache, v_cache, slot_mapping, stream=None):
-    """reshape_and_cache, or reshape_and_cache_fp8 with the workload's scales."""
+def write_rows(wl, k, v, k_cache, v_cache, slot_mapping, stream=None, scales=None):
+    """reshape_and_cache, or reshape_and_cache_fp8 with the workload's scales
+    (``scales``: the (k, v) scale arguments already converted, else converted here)."""
     if wl.kv_dtype == "fp8e4m3":
-        pkv.reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, wl.k_scale, wl.v_scale, stream=stream)
+        ks, vs = scales if scales is not None else (scale_arg(wl.k_scale, k.device), scale_arg(wl.v_scale, k.device))
+        pkv.reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, ks, vs, stream=stream)
     else:
         pkv.reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, stream=stream)
 
 
-def _flush(wl, chunks, k_cache, v_cache, dtype, device):
+def _flush(wl, chunks, k_cache, v_cache, dtype, device, scales=None):
     import torch
     if not chunks:
         return
@@ -141,7 +155,7 @@ def _flush(wl, chunks, k_cache, v_cache, dtype, device):
     k = np.concatenate([c[1] for c in chunks])
     v = np.concatenate([c[2] for c in chunks])
     write_rows(wl, to_device(k, dtype, device), to_device(v, dtype, device), k_cache, v_cache,
-               torch.from_numpy(slots).to(device))
+               torch.from_numpy(slots).to(device), scales=scales)
     chunks.clear()
 
 
@@ -164,6 +178,7 @@ def build_step(wl: synth.Workload, device="cuda", *, garbage: str = "nan", garba
     fp8 = wl.kv_dtype == "fp8e4m3"
     cdt = torch.uint8 if fp8 else tdt
     k_cache, v_cache = pkv.allocate_cache(wl.pool_blocks, hkv, cdt, device)
+    scales = (scale_arg(wl.k_scale, device), scale_arg(wl.v_scale, device)) if fp8 else (1.0, 1.0)
     bits = torch.uint8 if fp8 else torch.int16  # the caches' raw element bits
     if garbage == "nan":  # all-ones bits: NaN in fp16, bf16 and E4M3
         k_cache.view(bits).fill_(-1 if not fp8 else 255)
@@ -204,9 +219,9 @@ def build_step(wl: synth.Workload, device="cuda", *, garbage: str = "nan", garba
             pending.append((slots, k, v))
             pending_tokens += slots.shape[0]
             if pending_tokens >= fill_chunk_tokens:
-                _flush(wl, pending, k_cache, v_cache, dtype, device)
+                _flush(wl, pending, k_cache, v_cache, dtype, device, scales)
                 pending_tokens = 0
-    _flush(wl, pending, k_cache, v_cache, dtype, device)
+    _flush(wl, pending, k_cache, v_cache, dtype, device, scales)
 
     slots, pairs = bm.step(step_seqs)
     S = wl.num_seqs
@@ -227,7 +242,7 @@ def build_step(wl: synth.Workload, device="cuda", *, garbage: str = "nan", garba
         k_new=to_device(k_new, dtype, device), v_new=to_device(v_new, dtype, device),
         workspace=torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None,
         partition_tokens=pt, max_blocks=max_blocks, block_tables_host=tables, slot_mapping_host=slots,
-        block_pairs_host=pairs)
+        block_pairs_host=pairs, k_scale=scales[0], v_scale=scales[1])
     if run:
         step.run_step()
     return step
@@ -249,6 +264,8 @@ class GpuPrefill:
     partition_tokens: int
     max_blocks: int
     block_tables_host: np.ndarray
+    k_scale: object = 1.0  # fp8 cache: the scales as the binding takes them (float or GPU tensor)
+    v_scale: object = 1.0
 
     @property
     def fp8(self) -> bool:
@@ -256,7 +273,7 @@ class GpuPrefill:
 
     def run(self, out=None, stream=None, block_tables=None, k_cache=None, v_cache=None):
         out = self.out if out is None else out
-        kw = dict(k_scale=self.wl.k_scale, v_scale=self.wl.v_scale) if self.fp8 else {}
+        kw = dict(k_scale=self.k_scale, v_scale=self.v_scale) if self.fp8 else {}
         pkv.paged_attn_prefill(out, self.q, self.k_cache if k_cache is None else k_cache,
                                self.v_cache if v_cache is None else v_cache,
                                self.block_tables if block_tables is None else block_tables, self.context_lens,
@@ -327,7 +344,8 @@ def build_prefill(wl, device="cuda", *, garbage: str = "nan", garbage_seed: int 
         context_lens=torch.from_numpy(wl.context_lens.astype(np.int32)).to(device),
         query_start=torch.from_numpy(wl.query_start.astype(np.int32)).to(device),
         workspace=torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None,
-        partition_tokens=partition_tokens, max_blocks=max_blocks, block_tables_host=tables)
+        partition_tokens=partition_tokens, max_blocks=max_blocks, block_tables_host=tables,
+        k_scale=scale_arg(wl.k_scale, device) if fp8 else 1.0, v_scale=scale_arg(wl.v_scale, device) if fp8 else 1.0)
     if run:
         pre.run()
     return pre
@@ -417,7 +435,7 @@ def run_prefix_cache(wl, *, cached: bool = True, first_pos=None, device="cuda") 
         mb = max(bm.num_seq_blocks(r) for r in seqs)
         tables = bm.block_table(seqs, mb)
         out = torch.empty((int(qs[-1]), wl.num_heads, 128), dtype=tdt, device=device)
-        scales = dict(k_scale=wl.k_scale, v_scale=wl.v_scale) if fp8 else {}
+        scales = dict(k_scale=scale_arg(wl.k_scale, device), v_scale=scale_arg(wl.v_scale, device)) if fp8 else {}
         pkv.paged_attn_prefill(out, to_device(q, wl.dtype, device), k_cache, v_cache,
                                torch.from_numpy(tables).to(device),
                                torch.from_numpy(ctx.astype(np.int32)).to(device),

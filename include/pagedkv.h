@@ -254,8 +254,9 @@ pkv_status gather_cache(void* k_out, void* v_out, const void* k_cache, const voi
  * A PKV_FP8_E4M3 cache stores one byte per element: the OCP 8-bit floating-
  * point E4M3 code (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
  * exponent field 0 holds subnormals (m/8) * 2^-6; no infinities; S.1111.111 is
- * NaN; largest finite magnitude 448).  K and V each have one float32 scale:
- * the value a K code stands for is E4M3(code) * k_scale, and likewise for V.
+ * NaN; largest finite magnitude 448).  K and V each have a float32 scale,
+ * one per cache or one per KV head: the value a K code of head h stands for
+ * is E4M3(code) * k_scale (or * k_head_scales[h]), and likewise for V.
  * Writing x gives the code nearest to the float32 quotient x / scale (one
  * correctly rounded float32 division), ties to the even mantissa, magnitudes
  * of 448 and beyond saturated to +-448, the sign of zero kept.  Queries,
@@ -276,8 +277,15 @@ pkv_status gather_cache(void* k_out, void* v_out, const void* k_cache, const voi
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t act_dtype; /* PKV_F16 or PKV_BF16: dtype of q, out and the new k/v rows */
-  float k_scale;     /* finite and > 0 */
-  float v_scale;     /* finite and > 0 */
+  float k_scale;     /* one K scale for the cache: finite and > 0 (ignored when k_head_scales is set) */
+  float v_scale;     /* one V scale for the cache: finite and > 0 (ignored when v_head_scales is set) */
+  /* Optional per-KV-head scales: NULL, or a device float32 array
+   * [num_kv_heads] whose element h is the scale of every K (V) row of KV head
+   * h in every block, replacing k_scale (v_scale).  4-byte aligned; the
+   * values must be finite and > 0 (caller's contract, checked under
+   * PKV_VALIDATE=1).  K and V choose independently. */
+  const float* k_head_scales;
+  const float* v_head_scales;
 } pkv_fp8_scales;
 
 /* reshape_and_cache into an fp8 cache: the rows (act_dtype) are encoded as

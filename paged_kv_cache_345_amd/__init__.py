@@ -59,7 +59,8 @@ class CacheDesc(ctypes.Structure):
 
 
 class Fp8Scales(ctypes.Structure):
-    _fields_ = [("act_dtype", _i32), ("k_scale", _fl), ("v_scale", _fl)]
+    _fields_ = [("act_dtype", _i32), ("k_scale", _fl), ("v_scale", _fl), ("k_head_scales", _vp),
+                ("v_head_scales", _vp)]
 
 
 _DP = ctypes.POINTER(CacheDesc)
@@ -216,10 +217,26 @@ def cache_desc(num_blocks: int, num_kv_heads: int, dtype) -> CacheDesc:
     return CacheDesc(int(num_blocks), BLOCK_SIZE, int(num_kv_heads), HEAD_SIZE, code)
 
 
-def fp8_scales(act_dtype, k_scale: float, v_scale: float) -> Fp8Scales:
-    """act_dtype: torch.float16 / torch.bfloat16 (or a PKV_* code) of q, out and the new rows."""
+def fp8_scales(act_dtype, k_scale, v_scale, num_kv_heads: Optional[int] = None) -> Fp8Scales:
+    """act_dtype: torch.float16 / torch.bfloat16 (or a PKV_* code) of q, out and
+    the new rows.  k_scale / v_scale: a float (one scale per cache), or a GPU
+    float32 tensor [num_kv_heads] of per-head scales (its pointer is passed)."""
     code = act_dtype if isinstance(act_dtype, int) else _code_of_dtype(act_dtype)
-    return Fp8Scales(int(code), float(k_scale), float(v_scale))
+
+    def one(x, name):
+        if hasattr(x, "data_ptr"):
+            torch = _torch()
+            ptr = _gpu(x, name, torch.float32, 1)
+            if num_kv_heads is not None and x.shape[0] != num_kv_heads:
+                raise ValueError(f"{name} must have num_kv_heads = {num_kv_heads} entries")
+            if _validate.enabled():
+                _validate.check_head_scales(x, name)
+            return 1.0, ptr
+        return float(x), None
+
+    ks, kp = one(k_scale, "k_scale")
+    vs, vp = one(v_scale, "v_scale")
+    return Fp8Scales(int(code), ks, vs, kp, vp)
 
 
 def _desc_of(k_cache) -> CacheDesc:
@@ -374,13 +391,15 @@ def paged_attn_decode_run(out, q, k_cache, v_cache, block_tables, context_lens, 
 
 
 def paged_attn_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
-                          num_kv_heads: int, k_scale: float, v_scale: float, *, partition_tokens: int = 0,
+                          num_kv_heads: int, k_scale, v_scale, *, partition_tokens: int = 0,
                           workspace=None, stream=None):
     """paged_attn_decode over an fp8 (E4M3, uint8) cache whose codes stand for
-    code value * k_scale (K) and code value * v_scale (V); q, out fp16/bf16."""
+    code value * k_scale (K) and code value * v_scale (V); q, out fp16/bf16.
+    A scale is a float (one per cache) or a GPU float32 tensor [num_kv_heads]
+    (one per KV head)."""
     ptrs, desc, S, Hq, mbps, ws_ptr, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                                              num_kv_heads, partition_tokens, workspace)
-    sc = fp8_scales(q.dtype, k_scale, v_scale)
+    sc = fp8_scales(q.dtype, k_scale, v_scale, desc.num_kv_heads)
     st = lib().paged_attn_decode_fp8(*ptrs, float(scale), int(num_kv_heads), int(S), int(Hq), mbps,
                                      ctypes.byref(desc), ctypes.byref(sc), int(partition_tokens), ws_ptr, ws_bytes,
                                      _stream_handle(stream))
@@ -389,12 +408,12 @@ def paged_attn_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, 
 
 
 def paged_attn_decode_run_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
-                              num_kv_heads: int, k_scale: float, v_scale: float, *, workspace,
+                              num_kv_heads: int, k_scale, v_scale, *, workspace,
                               partition_tokens: int = 0, stream=None):
     """paged_attn_decode_fp8 from a work list written by paged_attn_decode_plan."""
     ptrs, desc, S, Hq, mbps, ws_ptr, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                                              num_kv_heads, partition_tokens, workspace)
-    sc = fp8_scales(q.dtype, k_scale, v_scale)
+    sc = fp8_scales(q.dtype, k_scale, v_scale, desc.num_kv_heads)
     st = lib().paged_attn_decode_run_fp8(*ptrs, float(scale), int(num_kv_heads), int(S), int(Hq), mbps,
                                          ctypes.byref(desc), ctypes.byref(sc), int(partition_tokens), ws_ptr,
                                          ws_bytes, _stream_handle(stream))
@@ -448,7 +467,7 @@ def paged_attn_prefill(out, q, k_cache, v_cache, block_tables, context_lens, que
             float(scale), int(num_kv_heads), int(num_seqs), int(num_heads), int(mbps), int(tq), int(max_query_len),
             ctypes.byref(desc)]
     if fp8:
-        sc = fp8_scales(q.dtype, k_scale, v_scale)
+        sc = fp8_scales(q.dtype, k_scale, v_scale, desc.num_kv_heads)
         st = lib().paged_attn_prefill_fp8(*args, ctypes.byref(sc), int(partition_tokens), ws_ptr, ws_bytes,
                                           _stream_handle(stream))
     else:
@@ -473,9 +492,11 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, stream=None):
     _check(st, "reshape_and_cache")
 
 
-def reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, k_scale: float, v_scale: float, *, stream=None):
+def reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale, *, stream=None):
     """Write the E4M3 codes of k[i] / k_scale and v[i] / v_scale (fp16/bf16 rows
-    [num_kv_heads, 128]) of every token i to slot_mapping[i] of a uint8 cache."""
+    [num_kv_heads, 128]) of every token i to slot_mapping[i] of a uint8 cache.
+    A scale is a float (one per cache) or a GPU float32 tensor [num_kv_heads]
+    (one per KV head)."""
     torch = _torch()
     desc = _desc_of(k_cache)
     n = int(slot_mapping.shape[0])
@@ -483,7 +504,7 @@ def reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, k_scale: float, 
         raise ValueError("k, v must be [num_tokens, num_kv_heads, 128]")
     if _validate.enabled():
         _validate.check_slots(slot_mapping, desc.num_blocks)
-    sc = fp8_scales(k.dtype, k_scale, v_scale)
+    sc = fp8_scales(k.dtype, k_scale, v_scale, desc.num_kv_heads)
     st = lib().reshape_and_cache_fp8(_gpu(k, "k"), _gpu(v, "v", k.dtype), _gpu(k_cache, "k_cache", torch.uint8),
                                      _gpu(v_cache, "v_cache", torch.uint8),
                                      _gpu(slot_mapping, "slot_mapping", torch.int32, 1), n, ctypes.byref(desc),

@@ -33,13 +33,28 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool is_fp8(const pkv_cache_desc* c) { return c->dtype == PKV_FP8_E4M3; }
 int32_t page_bytes(const pkv_cache_desc* c) { return is_fp8(c) ? pkv::kPageBytesFp8 : 2 * pkv::kPageElems; }
 
-// The scales of an fp8 call: act dtype fp16/bf16, finite positive scales.
+// The scales of an fp8 call: act dtype fp16/bf16; each of K and V has either
+// a per-head array (4-byte aligned device pointer) or a finite positive scalar.
 pkv_status check_scales(const pkv_fp8_scales* f) {
   if (!f) return PKV_ERR_INVALID;
   if (f->act_dtype != PKV_F16 && f->act_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-  if (!std::isfinite(f->k_scale) || !std::isfinite(f->v_scale) || !(f->k_scale > 0.f) || !(f->v_scale > 0.f))
-    return PKV_ERR_INVALID;
+  auto ok = [](float x, const float* per_head) {
+    if (per_head) return (reinterpret_cast<uintptr_t>(per_head) & 3u) == 0;
+    return std::isfinite(x) && x > 0.f;
+  };
+  if (!ok(f->k_scale, f->k_head_scales) || !ok(f->v_scale, f->v_head_scales)) return PKV_ERR_INVALID;
   return PKV_OK;
+}
+
+// Logit scale (log2 units) and output scale of a decode or prefill call; the
+// per-head arrays, when given, are applied in the kernels instead.
+void set_scales(pkv::DecodeArgs& a, float scale, const pkv_fp8_scales* fp8) {
+  const bool k_fold = fp8 && !fp8->k_head_scales;
+  a.scale_log2e = static_cast<float>(static_cast<double>(scale) * kLog2e *
+                                     (k_fold ? static_cast<double>(fp8->k_scale) : 1.0));
+  a.out_scale = fp8 && !fp8->v_head_scales ? fp8->v_scale : 1.0f;
+  a.k_head_scales = fp8 ? fp8->k_head_scales : nullptr;
+  a.v_head_scales = fp8 ? fp8->v_head_scales : nullptr;
 }
 
 // MI355X: 256 compute units; work-groups of the decode kernels that fit on one
@@ -240,8 +255,7 @@ pkv_status decode_impl(bool plan_first, void* out, const void* q, const void* k_
   a.ws_o = L.parts > 1 ? reinterpret_cast<float*>(ws + L.partial_o) : nullptr;
   a.ws_ml = L.parts > 1 ? reinterpret_cast<float*>(ws + L.partial_ml) : nullptr;
   a.plan = L.planned ? reinterpret_cast<int*>(ws + L.plan) : nullptr;
-  a.scale_log2e = static_cast<float>(static_cast<double>(scale) * kLog2e * (fp8 ? static_cast<double>(fp8->k_scale) : 1.0));
-  a.out_scale = fp8 ? fp8->v_scale : 1.0f;
+  set_scales(a, scale, fp8);
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
@@ -405,7 +419,7 @@ pkv_status write_impl(const void* k, const void* v, void* k_cache, void* v_cache
     hipError_t e = fp8 ? pkv::launch_reshape_and_cache_fp8(kt, vt, k_cache, v_cache, slot_mapping + t0, n,
                                                           cache->num_kv_heads, cache->num_blocks,
                                                           fp8->act_dtype == PKV_F16 ? 0 : 1, fp8->k_scale,
-                                                          fp8->v_scale, hs)
+                                                          fp8->v_scale, fp8->k_head_scales, fp8->v_head_scales, hs)
                        : pkv::launch_reshape_and_cache(kt, vt, k_cache, v_cache, slot_mapping + t0, n,
                                                       cache->num_kv_heads, cache->num_blocks, hs);
     if (e != hipSuccess) return PKV_ERR_DEVICE;
@@ -629,8 +643,7 @@ pkv_status prefill_impl(void* out, const void* q, const void* k_cache, const voi
   a.ws_o = P.parts > 1 ? reinterpret_cast<float*>(ws + P.partial_o) : nullptr;
   a.ws_ml = P.parts > 1 ? reinterpret_cast<float*>(ws + P.partial_ml) : nullptr;
   a.plan = nullptr;
-  a.scale_log2e = static_cast<float>(static_cast<double>(scale) * kLog2e * (fp8 ? static_cast<double>(fp8->k_scale) : 1.0));
-  a.out_scale = fp8 ? fp8->v_scale : 1.0f;
+  set_scales(a, scale, fp8);
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;

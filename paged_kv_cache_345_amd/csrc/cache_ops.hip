@@ -24,7 +24,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 }
 
 // fp8 (E4M3) cache write: the same work split; each element is encoded as
-// e4m3_encode(x / scale) with one correctly rounded float division.  K lands
+// e4m3_encode(x / scale) with one correctly rounded float division, scale
+// being the call's one K (V) scale or that of the element's KV head.  K lands
 // as one 8-byte store per lane (8 consecutive dims of one token are contiguous
 // in the fp8 K page).  A complete quad's V codes are staged in LDS and leave as
 // 32 16-byte stores per head page (dims 64a + b + {0, 16, 32, 48} of the 4
@@ -34,7 +35,8 @@ template <class DT>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint8_t* __restrict__ k_cache,
     uint8_t* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int64_t num_tokens, int num_kv_heads,
-    int64_t num_slots, float k_scale, float v_scale) {
+    int64_t num_slots, float k_scale, float v_scale, const float* __restrict__ k_head_scales,
+    const float* __restrict__ v_head_scales) {
   __shared__ uint2 stage[4][4][16];  // [quad token][head in group][chunk]: V codes
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int64_t q;
@@ -45,8 +47,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   const int h = 4 * hg + hh;
   const int32_t slot = w.slot(wave);
   const int64_t token = w.first + wave;
+  // this lane's head: its scales (per cache, or per KV head)
+  const bool head_ok = h < num_kv_heads;
+  if (head_ok && k_head_scales) k_scale = k_head_scales[h];
+  if (head_ok && v_head_scales) v_scale = v_head_scales[h];
 
-  if (slot >= 0 && h < num_kv_heads) {
+  if (slot >= 0 && head_ok) {
     const int64_t row = token * num_kv_heads + h;
     const int t = slot & 15;
     const int64_t page = (static_cast<int64_t>(slot >> 4) * num_kv_heads + h) * kPageBytesFp8;
@@ -243,6 +249,7 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
 hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
                                         const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                                         int32_t num_blocks, int act_dtype, float k_scale, float v_scale,
+                                        const float* k_head_scales, const float* v_head_scales,
                                         hipStream_t stream) {
   // one work-group per (window of 4 tokens, group of 4 KV heads), as above
   const int64_t items = (static_cast<int64_t>(num_tokens) + 3) / 4 * ((num_kv_heads + 3) / 4);
@@ -254,10 +261,10 @@ hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_ca
   const int64_t slots = static_cast<int64_t>(num_blocks) * kBlockSize;
   if (act_dtype == 0)
     reshape_and_cache_fp8_kernel<F16><<<g, b, 0, stream>>>(kk, vv, kc, vc, slot_mapping, num_tokens, num_kv_heads,
-                                                            slots, k_scale, v_scale);
+                                                            slots, k_scale, v_scale, k_head_scales, v_head_scales);
   else
     reshape_and_cache_fp8_kernel<BF16><<<g, b, 0, stream>>>(kk, vv, kc, vc, slot_mapping, num_tokens, num_kv_heads,
-                                                             slots, k_scale, v_scale);
+                                                             slots, k_scale, v_scale, k_head_scales, v_head_scales);
   return hipGetLastError();
 }
 

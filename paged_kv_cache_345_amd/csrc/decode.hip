@@ -151,6 +151,7 @@ __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(D
   }
   const int row_s = s, j_begin = wr.j0, j_count = wr.nb, nseg = wr.nseg;
   const int L = clamped_len(a, row_s);
+  const float sl2e = head_logit_scale(a, h);  // MHA: the unit is the KV head
   uint16_t* out_row = a.out + (static_cast<int64_t>(row_s) * a.num_heads + h) * kHeadSize;
   const int grp = lane >> 4;
   const int col = lane & 15;
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(D
 #pragma unroll
       for (int i = 0; i < 4; ++i) part = dot8<DT>(qf[i], kv[i], part);
       part = cross_row_sum(part);
-      const float x = (!kTail || col < nvalid) ? part * a.scale_log2e : kMaskedLogit;
+      const float x = (!kTail || col < nvalid) ? part * sl2e : kMaskedLogit;
 
       // online softmax with a wave-uniform running max
       const float m_new = fmaxf(m, row_max16(x));
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(256, DT::kMhaWavesPerSimd) void decode_mha_kernel(D
       O = fmaf(c, red_o[w][d], O);
     }
     if (nseg == 1) {
-      out_row[d] = DT::from_f32(O / Z * a.out_scale);
+      out_row[d] = DT::from_f32(O / Z * head_out_scale(a, h));
     } else {
       const int64_t slot = (static_cast<int64_t>(s) * a.num_heads + h) * a.parts_max + g;
       a.ws_o[slot * kHeadSize + d] = O;
@@ -266,6 +267,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   const int nh = min(16, a.group - tile * 16);
   const int grp = lane >> 4;
   const int col = lane & 15;
+  const float sl2e = head_logit_scale(a, kvh);
 
   const int L = clamped_len(a, s);
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
       for (int i = 0; i < 4; ++i) S = DT::mfma_qk(kv[i], qf[i], S);
       float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = (!kTail || 4 * grp + r < nvalid) ? S[r] * a.scale_log2e : kMaskedLogit;
+      for (int r = 0; r < 4; ++r) x[r] = (!kTail || 4 * grp + r < nvalid) ? S[r] * sl2e : kMaskedLogit;
 
       float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       bm = cross_row_max(bm);
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     if (wr.nseg == 1) {
       uint16_t* orow = out_seq + static_cast<int64_t>(h0 + hh) * kHeadSize + d0;
       uint4 packed;
-      const float os = a.out_scale;
+      const float os = head_out_scale(a, kvh);
       packed.x = DT::pack2(o[0] / Z * os, o[1] / Z * os);
       packed.y = DT::pack2(o[2] / Z * os, o[3] / Z * os);
       packed.z = DT::pack2(o[4] / Z * os, o[5] / Z * os);
@@ -415,8 +417,9 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   const int n = (nblk + a.blocks_per_part - 1) / a.blocks_per_part;
   if (n <= 1) return;  // written directly by the decode kernel
   const int64_t base = row * a.parts_max;
-  lse_merge_row<DT>(a.ws_ml + 2 * base, a.ws_o + base * kHeadSize, n, a.out + row * kHeadSize, a.out_scale,
-                    threadIdx.x & (kWave - 1));
+  const int kvh = static_cast<int>(row % a.num_heads) / a.group;
+  lse_merge_row<DT>(a.ws_ml + 2 * base, a.ws_o + base * kHeadSize, n, a.out + row * kHeadSize,
+                    head_out_scale(a, kvh), threadIdx.x & (kWave - 1));
 }
 
 template <class DT, class PF>

@@ -152,6 +152,15 @@ __device__ __attribute__((always_inline)) inline void stream_blocks(const Decode
   }
 }
 
+// The logit scale (log2 units) and the output scale of the rows of KV head
+// kvh: the call's scalars, or the fp8 cache's per-head K / V scales.
+__device__ inline float head_logit_scale(const DecodeArgs& a, int kvh) {
+  return a.k_head_scales ? a.scale_log2e * a.k_head_scales[kvh] : a.scale_log2e;
+}
+__device__ inline float head_out_scale(const DecodeArgs& a, int kvh) {
+  return a.v_head_scales ? a.v_head_scales[kvh] : a.out_scale;
+}
+
 // Merge of the n >= 2 segment partials of one output row by one wave:
 //   M = max_p m_p,  c_p = 2^(m_p - M),  out = sum_p c_p O_p / sum_p c_p Z_p.
 // ml: (m_p, Z_p) pairs; o: the partial rows, 128 floats each.  A segment in

@@ -34,8 +34,10 @@ struct DecodeArgs {
   float* ws_o;     // [S, Hq, parts_max, 128] unnormalised partial outputs
   float* ws_ml;    // [S, Hq, parts_max, 2]   (running max in log2 units, Z)
   int* plan;       // work-list plan (planned mode) or null
-  float scale_log2e;  // logit scale (times the K scale of an fp8 cache) in log2 units
-  float out_scale;    // 1, or the V scale of an fp8 cache
+  float scale_log2e;  // logit scale (times the one K scale of an fp8 cache) in log2 units
+  float out_scale;    // 1, or the one V scale of an fp8 cache
+  const float* k_head_scales;  // fp8 cache with per-KV-head K scales, else null: logits of head h * [h]
+  const float* v_head_scales;  // fp8 cache with per-KV-head V scales, else null: outputs of head h * [h]
   int num_seqs;
   int num_heads;
   int num_kv_heads;
@@ -114,6 +116,7 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
 hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
                                         const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                                         int32_t num_blocks, int act_dtype, float k_scale, float v_scale,
+                                        const float* k_head_scales, const float* v_head_scales,
                                         hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
                               int32_t num_kv_heads, int32_t num_blocks, int32_t page_bytes, hipStream_t stream);

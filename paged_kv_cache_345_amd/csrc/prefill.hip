@@ -269,8 +269,9 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
   // flipped, exact) the scores change sign exactly, and S sc = (-S)(-sc), so
   // every logit keeps its bits while the scale the steps use is >= 0 and the
   // row maximum of the logits is sc times the row maximum of the scores.
-  const bool neg_scale = a.scale_log2e < 0.f;
-  const float sc = neg_scale ? -a.scale_log2e : a.scale_log2e;
+  const float sl2e = head_logit_scale(a, kvh);
+  const bool neg_scale = sl2e < 0.f;
+  const float sc = neg_scale ? -sl2e : sl2e;
   if (neg_scale) {
 #pragma unroll
     for (int T = 0; T < kPrefillTiles; ++T)
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(256, kPrefillGroupsPerCu) void prefill_kernel(Prefi
       const int64_t orow = static_cast<int64_t>(q0 + row_query(T, tr)) * a.num_heads + h0 + tr % hpt;
       if (nseg == 1) {
         uint16_t* dst = a.out + orow * kHeadSize + col;
-        const float inv = a.out_scale / Zr;
+        const float inv = head_out_scale(a, kvh) / Zr;
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) dst[16 * jd] = DT::from_f32(O[T][jd][r] * inv);
       } else {
@@ -592,8 +593,9 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs pa) {
   const int n = (nblk + a.blocks_per_part - 1) / a.blocks_per_part;
   if (n <= 1) return;  // written directly by the prefill kernel
   const int64_t base = row * a.parts_max;
-  lse_merge_row<DT>(a.ws_ml + 2 * base, a.ws_o + base * kHeadSize, n, a.out + row * kHeadSize, a.out_scale,
-                    threadIdx.x & (kWave - 1));
+  const int kvh = static_cast<int>(row % a.num_heads) / a.group;
+  lse_merge_row<DT>(a.ws_ml + 2 * base, a.ws_o + base * kHeadSize, n, a.out + row * kHeadSize,
+                    head_out_scale(a, kvh), threadIdx.x & (kWave - 1));
 }
 
 template <class DT, class PF>

@@ -127,3 +127,11 @@ def check_prologue_sources(block_pairs, slot_mapping) -> None:
         if extra:
             raise ValueError(f"block_pairs ({src}, {dst}): tokens are written into the source block at offsets "
                              f"{sorted(extra)} that the destination does not receive")
+
+
+def check_head_scales(scales, name: str) -> None:
+    """Per-KV-head fp8 scales: finite and > 0."""
+    x = _host(scales).astype(np.float64)
+    bad = np.nonzero(~np.isfinite(x) | (x <= 0))[0]
+    if bad.size:
+        raise ValueError(f"{name}[{int(bad[0])}] = {x[bad[0]]} is not a finite positive scale")

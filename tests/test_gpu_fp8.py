@@ -198,3 +198,73 @@ def test_full_size_every_row(name):
     errs = fullsize.decode_errors(wl, got)
     worst = fullsize.report(name, errs, TOL[wl.dtype], f"all {wl.num_seqs} x {wl.num_heads} rows")
     assert worst <= TOL[wl.dtype]
+
+
+# --- per-KV-head scales ---------------------------------------------------
+
+HEAD_K = (0.012, 0.05, 0.02)
+HEAD_V = (0.03, 0.011, 0.02)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("kind", ["both", "k_only", "v_only"])
+def test_per_head_write_and_step_bit_exact(dtype, kind):
+    """A whole decode step with per-head K and/or V scales (the other one per
+    cache), from random garbage: every code equal to the oracle's, which
+    divides each head's rows by that head's scale."""
+    ks = HEAD_K if kind != "v_only" else 0.02
+    vs = HEAD_V if kind != "k_only" else 0.02
+    wl = _wl(3600 + len(kind) + (dtype == "bf16"), dtype=dtype, hkv=3, num_seqs=9, max_len=90, groups=2, ks=ks,
+             vs=vs, key_scale=(0.5, 2.0))
+    rng = np.random.default_rng(7)
+    shape = (wl.pool_blocks, 16, wl.num_kv_heads, 128)
+    gk = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    gv = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    step = harness.build_step(wl, garbage="pages", initial_pages=(encode_pages(gk, "k", fp8=True),
+                                                                  encode_pages(gv, "v", fp8=True)))
+    torch.cuda.synchronize()
+    ref = oracle.run_decode_step(wl, initial_cache=(gk, gv))
+    assert np.array_equal(decode_pages(step.k_cache.cpu().numpy(), "k", fp8=True), ref.k_cache)
+    assert np.array_equal(decode_pages(step.v_cache.cpu().numpy(), "v", fp8=True), ref.v_cache)
+    got = _out_f64(step.out, dtype)
+    assert np.abs(got - ref.out).max() <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("g", [1, 4, 16])
+@pytest.mark.parametrize("pt", [0, 32])
+def test_per_head_decode_matches_oracle(dtype, g, pt):
+    """Decode (MHA and GQA kernels, split segments merged by the reduce
+    kernel) over an fp8 cache with per-head K and V scales."""
+    wl = _wl(3700 + 10 * g + pt + (dtype == "bf16"), dtype=dtype, g=g, hkv=3 if g < 16 else 2, max_len=600,
+             ks=HEAD_K if g < 16 else HEAD_K[:2], vs=HEAD_V if g < 16 else HEAD_V[:2], key_scale=(0.5, 2.0))
+    step = harness.build_step(wl, partition_tokens=pt)
+    ref = oracle.run_decode_step(wl)
+    got = _out_f64(step.out, dtype)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref.out).max() <= TOL[dtype]
+
+
+def test_per_head_scales_equal_to_one_scale_are_bit_identical():
+    """Per-head arrays holding one value give bit-identical codes and outputs
+    to that value passed as the one scale per cache."""
+    a = _wl(3800, dtype="bf16", g=4, hkv=3, max_len=400, ks=0.02, vs=0.03, key_scale=(0.5, 2.0))
+    b = _wl(3800, dtype="bf16", g=4, hkv=3, max_len=400, ks=(0.02,) * 3, vs=(0.03,) * 3, key_scale=(0.5, 2.0))
+    sa, sb = harness.build_step(a), harness.build_step(b)
+    torch.cuda.synchronize()
+    assert torch.equal(sa.k_cache, sb.k_cache) and torch.equal(sa.v_cache, sb.v_cache)
+    assert torch.equal(sa.out.view(torch.int16), sb.out.view(torch.int16))
+
+
+def test_per_head_scale_validation(monkeypatch):
+    wl = _wl(3900, dtype="fp16", hkv=3, max_len=50, ks=HEAD_K, vs=HEAD_V)
+    step = harness.build_step(wl)
+    bad = torch.tensor([0.01, 0.02], dtype=torch.float32, device="cuda")  # two entries for three heads
+    with pytest.raises(ValueError):
+        pkv.paged_attn_decode_fp8(torch.empty_like(step.out), step.q, step.k_cache, step.v_cache, step.block_tables,
+                                  step.context_lens, wl.scale, 3, bad, 0.02)
+    monkeypatch.setenv("PKV_VALIDATE", "1")
+    neg = torch.tensor([0.01, -0.02, 0.02], dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="finite positive"):
+        pkv.paged_attn_decode_fp8(torch.empty_like(step.out), step.q, step.k_cache, step.v_cache, step.block_tables,
+                                  step.context_lens, wl.scale, 3, neg, 0.02)

@@ -105,11 +105,13 @@ def test_stale_slots_and_block_ids_do_not_matter(g):
     assert torch.equal(out.view(torch.int16), a.out.view(torch.int16))
 
 
-@pytest.mark.parametrize("dtype,g", [("fp16", 1), ("bf16", 8)])
-def test_fp8_cache(dtype, g):
-    wl = synth.make_prefill_workload(8300 + g, num_seqs=4, num_heads=2 * g, num_kv_heads=2, dtype=dtype,
-                                     context=(1, 300), chunk=(1, 80), kv_dtype="fp8e4m3", k_scale=0.0125,
-                                     v_scale=0.02)
+@pytest.mark.parametrize("dtype,g,per_head", [("fp16", 1, False), ("bf16", 8, False), ("fp16", 1, True),
+                                              ("bf16", 4, True)])
+def test_fp8_cache(dtype, g, per_head):
+    ks, vs = ((0.01, 0.03), (0.02, 0.012)) if per_head else (0.0125, 0.02)
+    wl = synth.make_prefill_workload(8300 + g + 10 * per_head, num_seqs=4, num_heads=2 * g, num_kv_heads=2,
+                                     dtype=dtype, context=(1, 300), chunk=(1, 80), kv_dtype="fp8e4m3", k_scale=ks,
+                                     v_scale=vs, key_scale=(0.5, 2.0) if per_head else None)
     pre = harness.build_prefill(wl, partition_tokens=64)
     got = _out_f64(pre.out, dtype)
     for (row, h), ref in _ref_rows(wl).items():
