@@ -78,7 +78,7 @@ def step_bytes(wl, step):
 
 DECODE_SOURCES = ("paged_kv_cache_345_amd/csrc/decode.hip", "paged_kv_cache_345_amd/csrc/pkv_device.h",
                   "paged_kv_cache_345_amd/csrc/pkv_launch.h", "paged_kv_cache_345_amd/csrc/api.hip",
-                  "paged_kv_cache_345_amd/csrc/plan.hip",
+                  "paged_kv_cache_345_amd/csrc/plan.hip", "paged_kv_cache_345_amd/csrc/plan_body.h",
                   "paged_kv_cache_345_amd/csrc/decode_common.h")
 
 
@@ -665,6 +665,24 @@ def main() -> int:
         f"({'flushed' if args.flush else 'not flushed'}; wall {wall_s / K * 1e6:.1f} us per step with the flush); "
         f"decode median {dec_med * 1e3:.1f} us, min {dec_min * 1e3:.1f} us, mean {dec_avg * 1e3:.1f} us")
 
+    # The page-read ceiling: the attention call's page reads alone (same work
+    # list, wave ranges and loads, no arithmetic), timed the same way.
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    step.plan()
+    rp_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        flush(i)
+        rp_ev[i][0].record()
+        pkv.paged_attn_decode_read_pages(step.k_cache, step.v_cache, step.block_tables, step.context_lens,
+                                         wl.num_heads, sink, workspace=step.workspace,
+                                         partition_tokens=step.partition_tokens)
+        rp_ev[i][1].record()
+    torch.cuda.synchronize()
+    rp_ms = np.array([a.elapsed_time(b) for a, b in rp_ev])
+    rp_med = float(np.median(rp_ms))
+    log(f"page reads alone: median {rp_med * 1e3:.1f} us, min {rp_ms.min() * 1e3:.1f} us "
+        f"({nb['decode'] / (rp_med * 1e-3) / 1e9:.0f} GB/s of the call's algorithmic bytes)")
+
     graph_us = None
     if args.graph:
         # the same step captured once in a HIP graph and replayed: no host
@@ -738,6 +756,14 @@ def main() -> int:
                    "events": "HIP events on the stream the kernels run on, around each step and each "
                              "paged_attn_decode_run call"},
         "graph_step_us": None if graph_us is None else round(graph_us, 2),
+        "page_read_ceiling": {
+            "what": ("paged_attn_decode_read_pages: the attention call's work list, wave ranges and page loads "
+                     "with no arithmetic, flushed and timed like the call"),
+            "us": {"median": round(rp_med * 1e3, 2), "min": round(float(rp_ms.min()) * 1e3, 2)},
+            "gbs": round(nb["decode"] / (rp_med * 1e-3) / 1e9, 2),
+            "frac_of_hbm_peak": round(nb["decode"] / (rp_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_call_over_ceiling": round(dec_med / rp_med, 4),
+        },
         "roofline": {
             "bound": "hbm",
             "kernel": ("paged_attn_decode_run: " + ("decode_mha_kernel" if wl.num_heads == wl.num_kv_heads

@@ -147,6 +147,22 @@ pkv_status paged_attn_decode_run(void* out, const void* q, const void* k_cache, 
                                  const pkv_cache_desc* cache, int32_t partition_tokens,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* paged_attn_decode_read_pages — a diagnostic: the page reads of
+ * paged_attn_decode_run alone.  With the work list that paged_attn_decode_plan
+ * wrote into `workspace` (same arguments), it runs the decode call's work
+ * items, wave ranges and load instructions over every live K and V page of
+ * the batch, with no dot products, softmax or output: its duration is the
+ * ceiling the memory system puts on paged_attn_decode_run for this batch
+ * ([repo] §2.1: the kernel's efficiency rests on how it reads the cache).
+ *   sink   device uint32, 16-byte aligned; written only in the (practically
+ *          never) case that the folded page words equal one fixed value.
+ * 16-bit or fp8 caches; errors as paged_attn_decode_run. */
+pkv_status paged_attn_decode_read_pages(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                        int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                        int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                        uint32_t* sink, void* stream);
+
 /* paged_attn_decode_noalloc — for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): the same call as paged_attn_decode without the workspace

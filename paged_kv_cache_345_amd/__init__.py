@@ -75,6 +75,7 @@ SIGNATURES = {
     "paged_attn_decode_plan": (_i32, [_vp, _i32, _i32, _i32, _DP, _i32, _vp, _sz, _vp]),
     "paged_attn_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _i32,
                                          _vp]),
+    "paged_attn_decode_read_pages": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _DP, _i32, _vp, _sz, _vp, _vp]),
     "paged_attn_decode_run": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _fl, _i32, _i32, _i32, _i32, _DP, _i32,
                                      _vp, _sz, _vp]),
     "paged_attn_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _DP]),
@@ -359,6 +360,25 @@ def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_le
                                          ctypes.byref(desc), int(partition_tokens), _stream_handle(stream))
     _check(st, "paged_attn_decode_noalloc")
     return out
+
+
+def paged_attn_decode_read_pages(k_cache, v_cache, block_tables, context_lens, num_heads: int, sink, *, workspace,
+                                 partition_tokens: int = 0, stream=None):
+    """Diagnostic: the page reads of paged_attn_decode_run alone, from the work
+    list paged_attn_decode_plan wrote into `workspace`; `sink` is a GPU int32
+    tensor of at least 4 elements."""
+    torch = _torch()
+    desc = _desc_of(k_cache)
+    num_seqs, mbps = block_tables.shape
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _gpu(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    st = lib().paged_attn_decode_read_pages(_gpu(k_cache, "k_cache"), _gpu(v_cache, "v_cache", k_cache.dtype),
+                                            _gpu(block_tables, "block_tables", torch.int32, 2),
+                                            _gpu(context_lens, "context_lens", torch.int32, 1), int(num_seqs),
+                                            int(num_heads), int(mbps), ctypes.byref(desc), int(partition_tokens),
+                                            ws_ptr, ws_bytes, _gpu(sink, "sink", torch.int32), _stream_handle(stream))
+    _check(st, "paged_attn_decode_read_pages")
 
 
 def paged_attn_decode_plan(context_lens, num_heads: int, max_blocks_per_seq: int, k_cache, workspace, *,

@@ -223,7 +223,7 @@ pkv_status decode_impl(bool plan_first, void* out, const void* q, const void* k_
                        const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t num_kv_heads,
                        int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
                        const pkv_fp8_scales* fp8, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       void* stream, uint32_t* read_probe_sink = nullptr) {
   pkv_status st = check_decode_shape(num_seqs, num_heads, max_blocks_per_seq, cache);
   if (st != PKV_OK) return st;
   // an fp8 cache comes only with its scales, and scales only with an fp8 cache
@@ -272,6 +272,7 @@ pkv_status decode_impl(bool plan_first, void* out, const void* q, const void* k_
     st = launch_plan(L, context_lens, num_seqs, num_heads, max_blocks_per_seq, workspace, hs);
     if (st != PKV_OK) return st;
   }
+  if (read_probe_sink) return from_hip(pkv::launch_decode_read_pages(a, fp8 != nullptr, read_probe_sink, hs));
   return from_hip(pkv::launch_decode(a, act_dtype == PKV_F16 ? 0 : 1, fp8 != nullptr, hs));
 }
 
@@ -365,6 +366,22 @@ pkv_status paged_attn_decode_noalloc(void* out, const void* q, const void* k_cac
   return decode_impl(true, out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, num_seqs,
                      num_heads, max_blocks_per_seq, cache, nullptr, partition_tokens, ws,
                      ws ? PKV_NOALLOC_SCRATCH_BYTES : 0, stream);
+}
+
+pkv_status paged_attn_decode_read_pages(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                        int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                        int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                        uint32_t* sink, void* stream) {
+  if (!sink || cache == nullptr) return PKV_ERR_INVALID;
+  // q and out are never touched: any aligned non-null pointers pass the shared checks
+  void* const unused = sink;
+  const bool fp8 = cache->dtype == PKV_FP8_E4M3;
+  pkv_fp8_scales ones{PKV_F16, 1.f, 1.f, nullptr, nullptr};
+  if ((reinterpret_cast<uintptr_t>(sink) & 15u) != 0) return PKV_ERR_INVALID;
+  return decode_impl(false, unused, unused, k_cache, v_cache, block_tables, context_lens, 1.f, cache->num_kv_heads,
+                     num_seqs, num_heads, max_blocks_per_seq, cache, fp8 ? &ones : nullptr, partition_tokens,
+                     workspace, workspace_bytes, stream, sink);
 }
 
 pkv_status paged_attn_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,

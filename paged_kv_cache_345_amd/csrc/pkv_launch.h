@@ -108,6 +108,7 @@ struct StepArgs {
 // act_dtype: 0 fp16, 1 bf16 (q, out); fp8_cache: the pages hold E4M3 codes
 hipError_t launch_decode(const DecodeArgs& a, int act_dtype, bool fp8_cache, hipStream_t stream);
 hipError_t launch_decode_plan(const PlanArgs& a, hipStream_t stream);
+hipError_t launch_decode_read_pages(const DecodeArgs& a, bool fp8_cache, uint32_t* sink, hipStream_t stream);
 hipError_t launch_decode_step_prologue(const StepArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int act_dtype, bool fp8_cache, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -5,6 +5,7 @@ Bit-exact cases: a context of one token (the output is that token's V),
 block-id permutations, stale-slot contents and repeated runs.
 """
 
+import ctypes
 import dataclasses
 
 import numpy as np
@@ -306,3 +307,26 @@ def test_many_sequences_planned_and_direct(num_seqs, g):
     for s in range(num_seqs):
         worst = max(worst, float(np.abs(got[s] - _ref_seq(wl, s)).max()))
     assert worst <= TOL["fp16"], worst
+
+
+@pytest.mark.parametrize("name,g", [("random", 1), ("random", 8), ("fp8", 4)])
+def test_read_pages_probe_runs_and_leaves_the_sink(name, g):
+    """The page-read diagnostic runs the decode call's loads over the planned
+    work list and writes nothing (its sink keeps its value unless the folded
+    page words hit one fixed value); it refuses a missing sink."""
+    kw = dict(kv_dtype="fp8e4m3", k_scale=0.02, v_scale=0.02) if name == "fp8" else {}
+    wl = synth.make_random_workload(9950 + g, num_seqs=7, num_heads=2 * g, num_kv_heads=2,
+                                    dtype="bf16" if g > 1 else "fp16", max_len=900, min_len=1, groups=1, **kw)
+    step = harness.build_step(wl, partition_tokens=64)
+    step.plan()
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    pkv.paged_attn_decode_read_pages(step.k_cache, step.v_cache, step.block_tables, step.context_lens,
+                                     wl.num_heads, sink, workspace=step.workspace, partition_tokens=64)
+    torch.cuda.synchronize()
+    assert (sink == 7).all()
+    desc = step.desc
+    st = pkv.lib().paged_attn_decode_read_pages(step.k_cache.data_ptr(), step.v_cache.data_ptr(),
+                                                step.block_tables.data_ptr(), step.context_lens.data_ptr(),
+                                                wl.num_seqs, wl.num_heads, step.max_blocks, ctypes.byref(desc), 64,
+                                                step.workspace.data_ptr(), step.workspace.numel(), None, None)
+    assert st == pkv.PKV_ERR_INVALID
