@@ -82,14 +82,19 @@ DECODE_SOURCES = ("paged_kv_cache_345_amd/csrc/decode.hip", "paged_kv_cache_345_
                   "paged_kv_cache_345_amd/csrc/decode_common.h")
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per paged_attn_decode call from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None
-    when there is no summary for this workload or the decode sources changed
-    since the counters were taken."""
+PREFILL_SOURCES = ("paged_kv_cache_345_amd/csrc/prefill.hip", "paged_kv_cache_345_amd/csrc/decode_common.h",
+                   "paged_kv_cache_345_amd/csrc/pkv_device.h", "paged_kv_cache_345_amd/csrc/pkv_launch.h",
+                   "paged_kv_cache_345_amd/csrc/api.hip")
+
+
+def measured_traffic(stem: str, sources=DECODE_SOURCES):
+    """HBM bytes per call from the committed rocprofv3 counter summary
+    profiles/<stem>_hbm_traffic.md (FETCH_SIZE + WRITE_SIZE, calibrated against
+    a plain copy), or None when there is no summary for this workload or the
+    kernel sources changed since the counters were taken."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{stem}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -98,7 +103,7 @@ def measured_traffic(workload: str):
             k, v = line.split(":", 1)
             fields[k] = v.strip()
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     if fields.get("sources_sha256") != h.hexdigest() or "traffic_bytes_per_call" not in fields:
@@ -335,10 +340,13 @@ def prefill_bench(args, name: str) -> int:
                                                           "mean": round(float(calls.mean()) * 1e3, 2)}},
         "query_tokens_per_s": round(int(C.sum()) / (call_ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "kernel": "paged_attn_prefill: prefill_kernel", "achieved": round(tflops, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": measured_traffic(name, PREFILL_SOURCES),
                      "hbm_gbs": round((kv_bytes + qo_bytes) / (call_ms * 1e-3) / 1e9, 1)},
         "cpu_baseline": None,
     }
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -773,7 +781,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(wl.spec.name),
+            "traffic": measured_traffic(f"decode_{wl.spec.name}"),
         },
         "cpu_baseline": None,
     }
