@@ -4,8 +4,9 @@
 One step = the GPU calls of a decode step over one synthetic batch with every
 input already resident in HBM: copy_blocks (copy-on-write pairs),
 reshape_and_cache (the new tokens) and paged_attn_decode_plan (the batch's work
-list), issued as one decode_step_prologue launch over a 16-bit cache, then
-paged_attn_decode_run (the attention; segments of long rows merged by the
+list), issued as one decode_step_prologue launch (decode_step_prologue_fp8
+over an fp8 cache), then paged_attn_decode_run (the attention; segments of
+long rows merged by the
 log-sum-exp reduce).  The roofline figure is for the attention run
 alone, timed with HIP events on the stream it runs on.
 Default workload: the LLaMA-13B-shaped batch (128 sequences, 40 MHA heads,
@@ -577,6 +578,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", dest="flush", action="store_false",
                     help="decode workloads: run the timed steps back to back, without the cache flush")
+    ap.add_argument("--separate-prologue", action="store_true",
+                    help="decode workloads: issue copy_blocks, the write and the plan as three calls instead of "
+                         "one decode_step_prologue launch")
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: also time the step captured in a HIP graph and replayed")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -638,7 +642,7 @@ def main() -> int:
             torch.sum(scratch.view(torch.int64), dim=0, keepdim=True, out=sink)
 
     def one_step():
-        if step.fp8:
+        if args.separate_prologue:
             step.copy()
             step.write()
             step.plan()
@@ -742,10 +746,10 @@ def main() -> int:
                                                          step.partition_tokens),
             "copy_pairs": int(step.block_pairs_host.shape[0]),
             "kv_cache_dtype": wl.kv_dtype,
-            "step": ("decode_step_prologue (copy_blocks + reshape_and_cache + paged_attn_decode_plan in one "
-                     "launch) + paged_attn_decode_run"
-                     if wl.kv_dtype == wl.dtype else
-                     "copy_blocks + reshape_and_cache_fp8 + paged_attn_decode_plan + paged_attn_decode_run_fp8"),
+            "step": (("copy_blocks + reshape_and_cache{0} + paged_attn_decode_plan + paged_attn_decode_run{0}"
+                      if args.separate_prologue else
+                      "decode_step_prologue{0} (copy_blocks + reshape_and_cache{0} + paged_attn_decode_plan in one "
+                      "launch) + paged_attn_decode_run{0}").format("_fp8" if step.fp8 else "")),
             "parallelism": "single GPU",
         },
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),

@@ -111,12 +111,17 @@ class GpuStep:
         pkv.paged_attn_decode_plan(self.context_lens, self.wl.num_heads, self.max_blocks, self.k_cache,
                                    self.workspace, partition_tokens=self.partition_tokens, stream=stream)
 
-    def prologue(self, stream=None):
-        """The copy, the write and the plan in one launch (decode_step_prologue;
-        16-bit caches)."""
-        pkv.decode_step_prologue(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slot_mapping,
-                                 self.block_pairs, self.context_lens, self.wl.num_heads, self.max_blocks,
-                                 self.workspace, partition_tokens=self.partition_tokens, stream=stream)
+    def prologue(self, stream=None, force_16bit_entry: bool = False):
+        """The copy, the write and the plan in one launch (decode_step_prologue,
+        or decode_step_prologue_fp8 with the step's scales for an fp8 cache;
+        force_16bit_entry sends an fp8 cache to the 16-bit entry, which refuses it)."""
+        args = (self.k_new, self.v_new, self.k_cache, self.v_cache, self.slot_mapping, self.block_pairs,
+                self.context_lens, self.wl.num_heads, self.max_blocks, self.workspace)
+        if self.fp8 and not force_16bit_entry:
+            pkv.decode_step_prologue_fp8(*args, self.k_scale, self.v_scale, partition_tokens=self.partition_tokens,
+                                         stream=stream)
+        else:
+            pkv.decode_step_prologue(*args, partition_tokens=self.partition_tokens, stream=stream)
 
     def run(self, out=None, stream=None):
         """Attention from the planned work list (paged_attn_decode_run[_fp8])."""

@@ -339,11 +339,11 @@ pkv_status paged_attn_decode_run_fp8(void* out, const void* q, const void* k_cac
  * SOURCE block of a pair lies at an offset that is also written in that
  * pair's destination.  A decode step satisfies it: the samples that share a
  * partial block append at the same position, the copies into their fresh
- * blocks and the last sample in place.  16-bit caches only
- * (PKV_ERR_UNSUPPORTED for an fp8 cache).  With more than 65,536 tokens the
- * three kernels are launched separately (the fused copy reads the whole slot
- * mapping per copied page).  num_pairs == 0, num_tokens == 0 and num_seqs == 0
- * are allowed. */
+ * blocks and the last sample in place.  16-bit caches (PKV_ERR_UNSUPPORTED
+ * for an fp8 cache: decode_step_prologue_fp8 below is its form).  With more
+ * than 65,536 tokens the three kernels are launched separately (the fused
+ * copy reads the whole slot mapping per copied page).  num_pairs == 0,
+ * num_tokens == 0 and num_seqs == 0 are allowed. */
 pkv_status decode_step_prologue(const void* k, const void* v, void* k_cache, void* v_cache,
                                 const int32_t* slot_mapping, int32_t num_tokens,
                                 const int32_t* block_pairs, int32_t num_pairs,
@@ -351,6 +351,20 @@ pkv_status decode_step_prologue(const void* k, const void* v, void* k_cache, voi
                                 int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
                                 int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                                 void* stream);
+/* The same for an fp8 cache: copy_blocks, then reshape_and_cache_fp8(k, v,
+ * slot_mapping, scales), then the plan, in one launch.  A copied page that
+ * receives new tokens gets their E4M3 codes from the same encoding as the
+ * write (each element divided by its row's scale, then rounded to E4M3), so
+ * the result is bit-identical to the three calls.  scales: as
+ * reshape_and_cache_fp8 (PKV_ERR_INVALID when null or for a 16-bit cache);
+ * everything else as decode_step_prologue. */
+pkv_status decode_step_prologue_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int32_t* slot_mapping, int32_t num_tokens,
+                                    const int32_t* block_pairs, int32_t num_pairs,
+                                    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                    int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                    const pkv_fp8_scales* scales, int32_t partition_tokens,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * paged_attn_prefill — multi-token-query attention over the paged cache, for

@@ -94,6 +94,8 @@ SIGNATURES = {
     "copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _DP, _vp]),
     "decode_step_prologue": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _DP, _i32, _vp,
                                     _sz, _vp]),
+    "decode_step_prologue_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _DP, _SP,
+                                        _i32, _vp, _sz, _vp]),
     "swap_blocks": (_i32, [_vp, _vp, _DP, _vp, _vp, _DP, _vp, _i32, _vp]),
     "gather_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _DP, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -549,12 +551,7 @@ def copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
     _check(st, "copy_blocks")
 
 
-def decode_step_prologue(k, v, k_cache, v_cache, slot_mapping, block_pairs, context_lens, num_heads: int,
-                         max_blocks_per_seq: int, workspace, *, partition_tokens: int = 0, stream=None):
-    """copy_blocks(block_pairs), reshape_and_cache(k, v, slot_mapping) and
-    paged_attn_decode_plan(context_lens, ...) into `workspace`, in one launch
-    (16-bit caches; see pagedkv.h for the one extra condition)."""
-    torch = _torch()
+def _prologue_args(k, v, k_cache, slot_mapping, block_pairs, context_lens, max_blocks_per_seq, workspace):
     desc = _desc_of(k_cache)
     n = int(slot_mapping.shape[0])
     if tuple(k.shape) != (n, desc.num_kv_heads, HEAD_SIZE) or tuple(v.shape) != tuple(k.shape):
@@ -574,6 +571,17 @@ def decode_step_prologue(k, v, k_cache, v_cache, slot_mapping, block_pairs, cont
     if workspace is not None:
         ws_ptr = _gpu(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
+    return desc, n, npairs, S, ws_ptr, ws_bytes
+
+
+def decode_step_prologue(k, v, k_cache, v_cache, slot_mapping, block_pairs, context_lens, num_heads: int,
+                         max_blocks_per_seq: int, workspace, *, partition_tokens: int = 0, stream=None):
+    """copy_blocks(block_pairs), reshape_and_cache(k, v, slot_mapping) and
+    paged_attn_decode_plan(context_lens, ...) into `workspace`, in one launch
+    (16-bit caches; see pagedkv.h for the one extra condition)."""
+    torch = _torch()
+    desc, n, npairs, S, ws_ptr, ws_bytes = _prologue_args(k, v, k_cache, slot_mapping, block_pairs, context_lens,
+                                                          max_blocks_per_seq, workspace)
     row_dtype = None if desc.dtype == PKV_FP8_E4M3 else k_cache.dtype  # fp8: the library refuses the cache
     st = lib().decode_step_prologue(_gpu(k, "k", row_dtype), _gpu(v, "v", row_dtype),
                                     _gpu(k_cache, "k_cache"), _gpu(v_cache, "v_cache", k_cache.dtype),
@@ -583,6 +591,26 @@ def decode_step_prologue(k, v, k_cache, v_cache, slot_mapping, block_pairs, cont
                                     int(max_blocks_per_seq), ctypes.byref(desc), int(partition_tokens), ws_ptr,
                                     ws_bytes, _stream_handle(stream))
     _check(st, "decode_step_prologue")
+
+
+def decode_step_prologue_fp8(k, v, k_cache, v_cache, slot_mapping, block_pairs, context_lens, num_heads: int,
+                             max_blocks_per_seq: int, workspace, k_scale, v_scale, *, partition_tokens: int = 0,
+                             stream=None):
+    """decode_step_prologue for an fp8 cache: copy_blocks, reshape_and_cache_fp8
+    with the scales (a float, or a GPU float32 tensor [num_kv_heads], each) and
+    the plan, in one launch; bit-identical to the three calls."""
+    torch = _torch()
+    desc, n, npairs, S, ws_ptr, ws_bytes = _prologue_args(k, v, k_cache, slot_mapping, block_pairs, context_lens,
+                                                          max_blocks_per_seq, workspace)
+    sc = fp8_scales(k.dtype, k_scale, v_scale, desc.num_kv_heads)
+    st = lib().decode_step_prologue_fp8(_gpu(k, "k"), _gpu(v, "v", k.dtype), _gpu(k_cache, "k_cache", torch.uint8),
+                                        _gpu(v_cache, "v_cache", torch.uint8),
+                                        _gpu(slot_mapping, "slot_mapping", torch.int32, 1), n,
+                                        _gpu(block_pairs, "block_pairs", torch.int32, 2) if npairs else None, npairs,
+                                        _gpu(context_lens, "context_lens", torch.int32, 1), S, int(num_heads),
+                                        int(max_blocks_per_seq), ctypes.byref(desc), ctypes.byref(sc),
+                                        int(partition_tokens), ws_ptr, ws_bytes, _stream_handle(stream))
+    _check(st, "decode_step_prologue_fp8")
 
 
 def swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, *, stream=None):
@@ -752,6 +780,7 @@ __all__ = [
     "workspace_size", "partition_tokens_for", "paged_attn_decode", "paged_attn_decode_plan",
     "paged_attn_decode_run", "reshape_and_cache", "copy_blocks", "PKV_FP8_E4M3", "Fp8Scales", "fp8_scales",
     "paged_attn_decode_fp8", "paged_attn_decode_run_fp8", "reshape_and_cache_fp8", "paged_attn_prefill",
-    "prefill_workspace_size", "swap_blocks",
+    "prefill_workspace_size", "swap_blocks", "decode_step_prologue", "decode_step_prologue_fp8",
+    "paged_attn_decode_noalloc", "paged_attn_decode_read_pages", "NOALLOC_SCRATCH_BYTES",
     "gather_cache", "BlockManager", "SIGNATURES",
 ]

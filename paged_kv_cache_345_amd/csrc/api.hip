@@ -506,14 +506,24 @@ bool step_plan_fits(const DecodeLayout& L, int32_t num_seqs) {
 
 extern "C" {
 
-pkv_status decode_step_prologue(const void* k, const void* v, void* k_cache, void* v_cache,
-                                const int32_t* slot_mapping, int32_t num_tokens, const int32_t* block_pairs,
-                                int32_t num_pairs, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                                int32_t max_blocks_per_seq, const pkv_cache_desc* cache, int32_t partition_tokens,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// decode_step_prologue and its fp8 form (fp8: the write's scales, null for a
+// 16-bit cache).
+pkv_status prologue_impl(const void* k, const void* v, void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                         int32_t num_tokens, const int32_t* block_pairs, int32_t num_pairs,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                         const pkv_cache_desc* cache, const pkv_fp8_scales* fp8, int32_t partition_tokens,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   pkv_status st = check_desc(cache);
   if (st != PKV_OK) return st;
-  if (is_fp8(cache)) return PKV_ERR_UNSUPPORTED;
+  if (is_fp8(cache) != (fp8 != nullptr)) return fp8 ? PKV_ERR_INVALID : PKV_ERR_UNSUPPORTED;
+  if (fp8) {
+    st = check_scales(fp8);
+    if (st != PKV_OK) return st;
+  }
   if (num_tokens < 0 || num_pairs < 0) return PKV_ERR_INVALID;
   DecodeLayout L;
   st = decode_layout(num_seqs, num_heads, max_blocks_per_seq, partition_tokens, cache, &L);
@@ -532,7 +542,7 @@ pkv_status decode_step_prologue(const void* k, const void* v, void* k_cache, voi
   // a bulk write keeps the separate kernels: the merge scans every token per copied page
   if (num_tokens > 65536) {
     st = copy_blocks(k_cache, v_cache, block_pairs, num_pairs, cache, stream);
-    if (st == PKV_OK) st = reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens, cache, stream);
+    if (st == PKV_OK) st = write_impl(k, v, k_cache, v_cache, slot_mapping, num_tokens, cache, fp8, stream);
     if (st == PKV_OK && plan) st = launch_plan(L, context_lens, num_seqs, num_heads, max_blocks_per_seq, workspace, hs);
     return st;
   }
@@ -549,6 +559,12 @@ pkv_status decode_step_prologue(const void* k, const void* v, void* k_cache, voi
   a.num_kv_heads = cache->num_kv_heads;
   a.num_blocks = cache->num_blocks;
   a.planned = fused_plan ? 1 : 0;
+  if (fp8) {
+    a.k_scale = fp8->k_scale;
+    a.v_scale = fp8->v_scale;
+    a.k_head_scales = fp8->k_head_scales;
+    a.v_head_scales = fp8->v_head_scales;
+  }
   if (fused_plan) {
     a.plan.context_lens = context_lens;
     a.plan.plan = reinterpret_cast<int*>(static_cast<char*>(workspace) + L.plan);
@@ -560,10 +576,36 @@ pkv_status decode_step_prologue(const void* k, const void* v, void* k_cache, voi
     a.plan.parts_max = L.parts;
     a.plan.scan = plan_scan_fits(num_seqs, L, pkv::kStepThreads) ? 1 : 0;
   }
-  st = from_hip(pkv::launch_decode_step_prologue(a, hs));
+  st = from_hip(pkv::launch_decode_step_prologue(a, fp8 != nullptr, fp8 && fp8->act_dtype == PKV_BF16 ? 1 : 0, hs));
   if (st == PKV_OK && plan && !fused_plan)
     st = launch_plan(L, context_lens, num_seqs, num_heads, max_blocks_per_seq, workspace, hs);
   return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status decode_step_prologue(const void* k, const void* v, void* k_cache, void* v_cache,
+                                const int32_t* slot_mapping, int32_t num_tokens, const int32_t* block_pairs,
+                                int32_t num_pairs, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                int32_t max_blocks_per_seq, const pkv_cache_desc* cache, int32_t partition_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return prologue_impl(k, v, k_cache, v_cache, slot_mapping, num_tokens, block_pairs, num_pairs, context_lens,
+                       num_seqs, num_heads, max_blocks_per_seq, cache, nullptr, partition_tokens, workspace,
+                       workspace_bytes, stream);
+}
+
+pkv_status decode_step_prologue_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int32_t* slot_mapping, int32_t num_tokens, const int32_t* block_pairs,
+                                    int32_t num_pairs, const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_heads, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                    const pkv_fp8_scales* scales, int32_t partition_tokens, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!scales) return PKV_ERR_INVALID;
+  return prologue_impl(k, v, k_cache, v_cache, slot_mapping, num_tokens, block_pairs, num_pairs, context_lens,
+                       num_seqs, num_heads, max_blocks_per_seq, cache, scales, partition_tokens, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -23,90 +23,15 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   write_rows16(blockIdx.x, k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, num_slots);
 }
 
-// fp8 (E4M3) cache write: the same work split; each element is encoded as
-// e4m3_encode(x / scale) with one correctly rounded float division, scale
-// being the call's one K (V) scale or that of the element's KV head.  K lands
-// as one 8-byte store per lane (8 consecutive dims of one token are contiguous
-// in the fp8 K page).  A complete quad's V codes are staged in LDS and leave as
-// 32 16-byte stores per head page (dims 64a + b + {0, 16, 32, 48} of the 4
-// tokens each); other tokens' V as eight 1-byte stores.  The K store policy
-// follows the 16-bit kernel above.
+// fp8 (E4M3) cache write: write_rows_fp8 (cache_write.h) per work-group.
 template <class DT>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint8_t* __restrict__ k_cache,
     uint8_t* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int64_t num_tokens, int num_kv_heads,
     int64_t num_slots, float k_scale, float v_scale, const float* __restrict__ k_head_scales,
     const float* __restrict__ v_head_scales) {
-  __shared__ uint2 stage[4][4][16];  // [quad token][head in group][chunk]: V codes
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int64_t q;
-  int hg;
-  if (!write_item(blockIdx.x, num_tokens, num_kv_heads, q, hg)) return;  // the whole work-group: no barrier is skipped
-  const WriteWindow w(slot_mapping, q, num_tokens, num_slots);
-  const int hh = lane >> 4, c = lane & 15;
-  const int h = 4 * hg + hh;
-  const int32_t slot = w.slot(wave);
-  const int64_t token = w.first + wave;
-  // this lane's head: its scales (per cache, or per KV head)
-  const bool head_ok = h < num_kv_heads;
-  if (head_ok && k_head_scales) k_scale = k_head_scales[h];
-  if (head_ok && v_head_scales) v_scale = v_head_scales[h];
-
-  if (slot >= 0 && head_ok) {
-    const int64_t row = token * num_kv_heads + h;
-    const int t = slot & 15;
-    const int64_t page = (static_cast<int64_t>(slot >> 4) * num_kv_heads + h) * kPageBytesFp8;
-    const uint4 kv = reinterpret_cast<const uint4*>(k + row * kHeadSize)[c];
-    uint2 kq = make_uint2(0u, 0u);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kq.x |= e4m3_encode(elem<DT>(kv, e) / k_scale) << (8 * e);
-      kq.y |= e4m3_encode(elem<DT>(kv, 4 + e) / k_scale) << (8 * e);
-    }
-    const __amdgpu_buffer_rsrc_t kr = range_rsrc(k_cache + page, kPageBytesFp8);
-    if (w.lone(wave))
-      store8<kNonTemporal>(kr, k_page_offset_fp8(t, 8 * c), kq);
-    else
-      store8(kr, k_page_offset_fp8(t, 8 * c), kq);
-    if (!w.in_quad(wave)) {
-      const uint4 vv = reinterpret_cast<const uint4*>(v + row * kHeadSize)[c];
-      const __amdgpu_buffer_rsrc_t vr = range_rsrc(v_cache + page, kPageBytesFp8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        store1(vr, v_page_offset_fp8(t, 8 * c + e), static_cast<uint8_t>(e4m3_encode(elem<DT>(vv, e) / v_scale)));
-    }
-  }
-  if (w.lead >= 0 && h < num_kv_heads) {  // quad token `wave`, head h, chunk c: encode into LDS
-    const int64_t row = (w.first + w.lead + wave) * num_kv_heads + h;
-    const uint4 vv = reinterpret_cast<const uint4*>(v + row * kHeadSize)[c];
-    uint2 vq = make_uint2(0u, 0u);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vq.x |= e4m3_encode(elem<DT>(vv, e) / v_scale) << (8 * e);
-      vq.y |= e4m3_encode(elem<DT>(vv, 4 + e) / v_scale) << (8 * e);
-    }
-    stage[wave][hh][c] = vq;
-  }
-  __syncthreads();
-  const int hw = 4 * hg + wave;  // this wave stores the quad's V page of head hw
-  if (w.lead >= 0 && hw < num_kv_heads && lane < 32) {
-    // lane (a = lane / 16, b = lane % 16): byte 8p + 4r + t of its chunk holds
-    // dim 64a + 32p + 16r + b of quad token t
-    const int a = lane >> 4, b = lane & 15;
-    uint32_t x[4];
-#pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {  // pr = 2p + r
-      const int d = 64 * a + 16 * pr + b;
-      uint32_t word = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        word |= static_cast<uint32_t>(reinterpret_cast<const uint8_t*>(stage[t][wave])[d]) << (8 * t);
-      x[pr] = word;
-    }
-    const int64_t page = (static_cast<int64_t>(w.lead_slot >> 4) * num_kv_heads + hw) * kPageBytesFp8;
-    store16(range_rsrc(v_cache + page, kPageBytesFp8), v_page_offset_fp8(w.lead_slot & 15, 64 * a + b),
-            make_uint4(x[0], x[1], x[2], x[3]));
-  }
+  write_rows_fp8<DT>(blockIdx.x, k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, num_slots, k_scale,
+                     v_scale, k_head_scales, v_head_scales);
 }
 
 // One work-group copies one page, 16 bytes per thread (256 threads for a

@@ -103,13 +103,18 @@ struct StepArgs {
   int planned;      // 1: the plan work-group writes the plan
   PlanArgs plan;
   int64_t plan_wg;  // the plan work-group: after the write work-groups, before the copies (set by the launcher)
+  // fp8 caches (k_cache / v_cache then hold E4M3 codes): the write's scales
+  float k_scale, v_scale;
+  const float* k_head_scales;  // [num_kv_heads] or null
+  const float* v_head_scales;
 };
 
 // act_dtype: 0 fp16, 1 bf16 (q, out); fp8_cache: the pages hold E4M3 codes
 hipError_t launch_decode(const DecodeArgs& a, int act_dtype, bool fp8_cache, hipStream_t stream);
 hipError_t launch_decode_plan(const PlanArgs& a, hipStream_t stream);
 hipError_t launch_decode_read_pages(const DecodeArgs& a, bool fp8_cache, uint32_t* sink, hipStream_t stream);
-hipError_t launch_decode_step_prologue(const StepArgs& a, hipStream_t stream);
+// fp8_cache: the pages hold E4M3 codes and the rows are act_dtype (0 fp16, 1 bf16)
+hipError_t launch_decode_step_prologue(const StepArgs& a, bool fp8_cache, int act_dtype, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int act_dtype, bool fp8_cache, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,

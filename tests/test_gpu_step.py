@@ -1,6 +1,7 @@
-"""The fused decode-step prologue (decode_step_prologue: the copy-on-write
-block copy, the slot-mapped write and the work-list plan in one launch)
-against the three separate calls.  Marked gpu.
+"""The fused decode-step prologue (decode_step_prologue and its fp8 form
+decode_step_prologue_fp8: the copy-on-write block copy, the slot-mapped write
+and the work-list plan in one launch) against the three separate calls.
+Marked gpu.
 
 Both start from the same caches (every prior token written, garbage in every
 other slot) and the same workspace contents; afterwards both whole caches,
@@ -9,9 +10,11 @@ bit-identical.  Batches: random shapes with parallel-sample groups of 2 to 9
 members (several copies of one source block, the last sample writing in
 place, prompts ending on a block boundary), padding slots, the LLaMA-13B-shaped
 batch at full size, and batch sizes on both sides of the fused plan's
-capacity and of the plan's own.  The cache contents after the step are the
-oracle's as well (tests/test_gpu_cache_ops.py checks the separate calls
-against the oracle bit for bit).
+capacity and of the plan's own; over fp8 caches the same with one scale per
+cache and one per KV head, fp16 and bf16 rows, and the LLaMA-13B- and
+GQA-shaped fp8 batches at full size.  The cache contents after the step are
+the oracle's as well (tests/test_gpu_cache_ops.py and tests/test_gpu_fp8.py
+check the separate calls against the oracle bit for bit).
 """
 
 import numpy as np
@@ -26,6 +29,10 @@ pytestmark = pytest.mark.gpu
 import paged_kv_cache_345_amd as pkv  # noqa: E402
 
 
+def _bits(t):
+    return t if t.dtype == torch.uint8 else t.view(torch.int16)
+
+
 def _pair(wl, pt=None):
     """Two copies of the same state before the step, with the same garbage."""
     a = harness.build_step(wl, garbage="random", garbage_seed=5, partition_tokens=pt, run=False)
@@ -34,7 +41,7 @@ def _pair(wl, pt=None):
         if st.workspace is not None:
             st.workspace.fill_(0x5A)
     torch.cuda.synchronize()
-    assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
+    assert torch.equal(_bits(a.k_cache), _bits(b.k_cache))
     return a, b
 
 
@@ -46,8 +53,8 @@ def _compare(a, b):
     b.prologue()
     oa, ob = a.run(out=torch.full_like(a.out, 7.0)), b.run(out=torch.full_like(b.out, 9.0))
     torch.cuda.synchronize()
-    assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
-    assert torch.equal(a.v_cache.view(torch.int16), b.v_cache.view(torch.int16))
+    assert torch.equal(_bits(a.k_cache), _bits(b.k_cache))
+    assert torch.equal(_bits(a.v_cache), _bits(b.v_cache))
     if a.workspace is not None:
         assert torch.equal(a.workspace, b.workspace)
     assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
@@ -107,12 +114,81 @@ def test_padding_slots_and_empty_parts():
     _compare(a, b)
 
 
-def test_fp8_cache_is_refused():
+def test_fp8_cache_is_refused_by_the_16bit_entry():
     wl = synth.make_random_workload(9800, num_seqs=3, num_heads=2, num_kv_heads=2, dtype="fp16", max_len=40,
                                     kv_dtype="fp8e4m3", k_scale=0.0125, v_scale=0.02)
     st = harness.build_step(wl, run=False)
     with pytest.raises(pkv.PagedKVError):
-        st.prologue()
+        st.prologue(force_16bit_entry=True)
+
+
+def test_fp8_entry_refuses_a_16bit_cache():
+    """The binding refuses the cache's dtype; the C entry point itself returns
+    PKV_ERR_INVALID for scales with a 16-bit cache, and for no scales."""
+    import ctypes
+
+    wl = synth.make_random_workload(9810, num_seqs=3, num_heads=2, num_kv_heads=2, dtype="fp16", max_len=40)
+    st = harness.build_step(wl, run=False)
+    with pytest.raises(TypeError):
+        pkv.decode_step_prologue_fp8(st.k_new, st.v_new, st.k_cache, st.v_cache, st.slot_mapping, st.block_pairs,
+                                     st.context_lens, wl.num_heads, st.max_blocks, st.workspace, 0.02, 0.02)
+    desc = st.desc
+    sc = pkv.fp8_scales(torch.float16, 0.02, 0.02)
+    ws = st.workspace
+    args = [st.k_new.data_ptr(), st.v_new.data_ptr(), st.k_cache.data_ptr(), st.v_cache.data_ptr(),
+            st.slot_mapping.data_ptr(), int(st.slot_mapping.shape[0]), None, 0, st.context_lens.data_ptr(),
+            wl.num_seqs, wl.num_heads, st.max_blocks, ctypes.byref(desc)]
+    tail = [0, None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel() * ws.element_size(), None]
+    assert pkv.lib().decode_step_prologue_fp8(*args, ctypes.byref(sc), *tail) == pkv.PKV_ERR_INVALID
+    assert pkv.lib().decode_step_prologue_fp8(*args, None, *tail) == pkv.PKV_ERR_INVALID
+    torch.cuda.synchronize()
+
+
+# per-KV-head scales of the fp8 batches below (3 KV heads)
+HEAD_K = (0.012, 0.05, 0.02)
+HEAD_V = (0.03, 0.011, 0.02)
+
+
+@pytest.mark.parametrize("gs,g,dtype,per_head", [(2, 1, "fp16", False), (3, 1, "bf16", True), (4, 4, "fp16", True),
+                                                 (9, 2, "bf16", False), (3, 8, "fp16", False)])
+def test_fp8_sample_groups(gs, g, dtype, per_head):
+    ks, vs = (HEAD_K, HEAD_V) if per_head else (0.0125, 0.02)
+    wl = synth.make_random_workload(9830 + 10 * gs + g, num_seqs=3 * gs + 7, num_heads=3 * g, num_kv_heads=3,
+                                    dtype=dtype, max_len=700, min_len=1, groups=3, group_size=gs,
+                                    kv_dtype="fp8e4m3", k_scale=ks, v_scale=vs)
+    a, b = _pair(wl)
+    assert a.block_pairs_host.shape[0] > 0
+    _compare(a, b)
+
+
+@pytest.mark.parametrize("num_seqs", [300, 1025])
+def test_fp8_plan_capacity_edges(num_seqs):
+    wl = synth.make_random_workload(9860 + num_seqs, num_seqs=num_seqs, num_heads=2, num_kv_heads=2, dtype="bf16",
+                                    max_len=60, min_len=1, groups=5, group_size=3, kv_dtype="fp8e4m3",
+                                    k_scale=0.0125, v_scale=0.0125)
+    a, b = _pair(wl)
+    _compare(a, b)
+
+
+def test_fp8_padding_slots():
+    wl = synth.make_random_workload(9870, num_seqs=9, num_heads=8, num_kv_heads=2, dtype="fp16", max_len=300,
+                                    min_len=1, groups=2, kv_dtype="fp8e4m3", k_scale=0.0125, v_scale=0.02)
+    a, b = _pair(wl)
+    sm = a.slot_mapping.clone()
+    sm[[1, 4]] = -1
+    for st in (a, b):
+        st.slot_mapping = sm
+    _compare(a, b)
+
+
+@pytest.mark.parametrize("name", ["llama13b_fp8", "gqa_fp8"])
+def test_fp8_full_size(name):
+    """The fp8 benchmark batches at full size (gqa_fp8: per-head K scales)."""
+    wl = synth.make_workload(name)
+    a, b = _pair(wl)
+    if name == "llama13b_fp8":
+        assert a.block_pairs_host.shape == (22, 2)
+    _compare(a, b)
 
 
 def test_validate_mode_checks_the_extra_condition(monkeypatch):
