@@ -208,3 +208,47 @@ def test_validate_mode_checks_the_extra_condition(monkeypatch):
     st.slot_mapping = torch.from_numpy(sm).cuda()
     with pytest.raises(ValueError, match="source block"):
         st.prologue()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_bulk_fallback_matches_the_three_calls(fp8):
+    """Past 65,536 tokens the prologue launches the copy, the write and the plan
+    as separate kernels: 70,000 new rows over 2 KV heads, copy pairs from
+    written blocks into blocks the write does not touch, and a 5-sequence plan,
+    against the three calls issued by hand (fp8: per-head K scales)."""
+    n, hkv, nb = 70_000, 2, 4_500
+    g = torch.Generator(device="cuda")
+    g.manual_seed(123)
+    rows = torch.randn((n, hkv, 128), generator=g, device="cuda").to(torch.bfloat16 if fp8 else torch.float16)
+    vrows = torch.randn((n, hkv, 128), generator=g, device="cuda").to(rows.dtype)
+    slots = torch.randperm(4_400 * 16, generator=g, device="cuda")[:n].to(torch.int32)
+    pairs = torch.tensor([[3, 4_450], [17, 4_451], [4_399, 4_499]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([1, 700, 2_048, 31, 16], dtype=torch.int32, device="cuda")
+    cdt = torch.uint8 if fp8 else torch.float16
+    ks = torch.tensor([0.0125, 0.05], dtype=torch.float32, device="cuda")
+    vs = 0.02
+    state = []
+    for _ in range(2):
+        kc, vc = pkv.allocate_cache(nb, hkv, cdt)
+        for c in (kc, vc):
+            c.view(torch.uint8).copy_(torch.randint(0, 256, c.view(torch.uint8).shape, generator=g.manual_seed(9),
+                                                    device="cuda", dtype=torch.uint8))
+        ws = torch.full((pkv.workspace_size(5, 4, 128, pkv.cache_desc(nb, hkv, cdt)),), 0x5A, dtype=torch.uint8,
+                        device="cuda")
+        state.append((kc, vc, ws))
+    (ka, va, wa), (kb, vb, wb) = state
+    pkv.copy_blocks(ka, va, pairs)
+    if fp8:
+        pkv.reshape_and_cache_fp8(rows, vrows, ka, va, slots, ks, vs)
+    else:
+        pkv.reshape_and_cache(rows, vrows, ka, va, slots)
+    pkv.paged_attn_decode_plan(lens, 4, 128, ka, wa)
+    args = (rows, vrows, kb, vb, slots, pairs, lens, 4, 128, wb)
+    if fp8:
+        pkv.decode_step_prologue_fp8(*args, ks, vs)
+    else:
+        pkv.decode_step_prologue(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(ka.view(torch.uint8), kb.view(torch.uint8))
+    assert torch.equal(va.view(torch.uint8), vb.view(torch.uint8))
+    assert torch.equal(wa, wb)
