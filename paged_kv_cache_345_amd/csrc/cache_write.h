@@ -179,14 +179,14 @@ __device__ inline uint32_t encode_fp8(const uint4& row8, int e, float scale) {
 }
 
 // The fp8 (E4M3) write of one work-group, write work-group `wg`: the same
-// work split; each element is encoded as e4m3_encode(x / scale) (encode_fp8
-// below) with one correctly rounded float division, scale
-// being the call's one K (V) scale or that of the element's KV head.  K lands
-// as one 8-byte store per lane (8 consecutive dims of one token are contiguous
-// in the fp8 K page).  A complete quad's V codes are staged in LDS and leave as
-// 32 16-byte stores per head page (dims 64a + b + {0, 16, 32, 48} of the 4
-// tokens each); other tokens' V as eight 1-byte stores.  The K store policy
-// follows the 16-bit kernel above.
+// work split; each element is encoded by encode_fp8 above (one correctly
+// rounded float division by the call's one K (V) scale or that of the
+// element's KV head, then e4m3_encode).  K lands as one 8-byte store per lane
+// (8 consecutive dims of one token are contiguous in the fp8 K page).  A
+// complete quad's V codes are staged in LDS and leave as 32 16-byte stores per
+// head page (dims 64a + b + {0, 16, 32, 48} of the 4 tokens each); other
+// tokens' V as eight 1-byte stores.  The K store policy follows write_rows16
+// above.
 template <class DT>
 __device__ inline void write_rows_fp8(int64_t wg, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                       uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
