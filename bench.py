@@ -282,6 +282,15 @@ def copy_probe(mib: int, reps: int = 3):
     log(f"copy probe: {reps} copies of {mib} MiB")
 
 
+def prefill_flops(context_lens, chunk_lens, num_heads: int) -> int:
+    """Algorithmic flops of a chunked-prefill call: chunk query j of sequence s
+    sits at position p = L_s - C_s + j and sees the p + 1 keys 0..p; each
+    (query, visible key, head) costs 2 * 128 flops for its score and 2 * 128
+    for its share of P V."""
+    visible = sum((2 * int(L) - int(C) + 1) * int(C) // 2 for L, C in zip(context_lens, chunk_lens))  # sum of p + 1
+    return visible * 4 * 128 * int(num_heads)
+
+
 def prefill_bench(args, name: str) -> int:
     """Chunked-prefill leg: one paged_attn_prefill call over a batch whose
     chunks attend causally to their paged prefixes.  Roofline: the matrix
@@ -316,8 +325,7 @@ def prefill_bench(args, name: str) -> int:
     log(f"prefill call median {call_ms * 1e3:.1f} us, min {calls.min() * 1e3:.1f} us, mean {calls.mean() * 1e3:.1f} us")
     L = wl.context_lens.astype(np.int64)
     C = wl.chunk_lens.astype(np.int64)
-    visible = int(sum(int(((L[s] - C[s] + 1) + L[s]) * C[s] // 2) for s in range(wl.num_seqs)))  # sum of p + 1
-    flops = visible * 4 * 128 * wl.num_heads
+    flops = prefill_flops(L, C, wl.num_heads)
     kv_bytes = int(L.sum()) * 2 * wl.num_kv_heads * 128 * (1 if wl.kv_dtype == "fp8e4m3" else 2)
     qo_bytes = 2 * int(C.sum()) * wl.num_heads * 128 * 2
     tflops = flops / (call_ms * 1e-3) / 1e12
