@@ -4,7 +4,8 @@ Marked gpu.
 Every call of the library is asynchronous on the caller's stream, allocates
 nothing and never synchronises, so a serving loop can capture a whole step
 (copy_blocks, reshape_and_cache, paged_attn_decode_plan, paged_attn_decode_run)
-once and replay it without host launch work.  Each replay must give the bits
+once and replay it without host launch work (the step's copy, write and plan
+also as one decode_step_prologue[_fp8] launch).  Each replay must give the bits
 of the eager step: the graph is replayed several times, with eager work of the
 program and synchronisations between replays, and every replay's output is
 compared with the eager result after the output buffer was overwritten.
@@ -40,25 +41,31 @@ def _decode_cases():
     }
 
 
+def _prologue(step, fused):
+    if fused:  # copy, write and plan in one launch
+        step.prologue()
+    else:
+        step.copy()
+        step.write()
+        step.plan()
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["three-calls", "fused-prologue"])
 @pytest.mark.parametrize("name", sorted(_decode_cases()))
-def test_decode_step_graph_replays_match_eager(name, monkeypatch):
+def test_decode_step_graph_replays_match_eager(name, fused, monkeypatch):
     monkeypatch.delenv("PKV_VALIDATE", raising=False)  # host checks copy to the host: not capturable
     make, pt = _decode_cases()[name]
     wl = make()
     step = harness.build_step(wl, partition_tokens=pt, run=False)
     # eager step
-    step.copy()
-    step.write()
-    step.plan()
+    _prologue(step, fused)
     eager = _bits(step.run())
     torch.cuda.synchronize()
 
     out_g = torch.empty_like(step.out)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        step.copy()
-        step.write()
-        step.plan()
+        _prologue(step, fused)
         step.run(out=out_g)
     torch.cuda.synchronize()
 
